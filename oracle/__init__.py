@@ -1,0 +1,58 @@
+"""CPU oracle for group-wise INT4 round-to-nearest quantization and the W4A16 product.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product
+path (``w4a16_decode_amd`` and its HIP library) never imports, calls or
+links it, and this package imports nothing from the product: the two share
+no code. Inputs for both come from ``synth``.
+
+Plain numpy, written for a reader to check against the source pages by eye:
+no blocking, fusion or reordering beyond what the formulas state.
+
+Sources, cited by page title and section throughout:
+
+[YBB]  "LLM 后训练量化深度实战：从 GPTQ/AWQ 到 FP8 与 KV Cache 量化的显存-带宽极限工程"
+       (www.ybb.press) -- section 二 (group-wise symmetric quantize_per_group and
+       its MSE demo), section 一 (roofline of the decode GEMV).
+[ARG]  "Post-training quantization: GPTQ, AWQ and rotation" (arganzheng.life,
+       part 03 of the efficient-inference series) -- section 二.2 (quantization
+       form, granularity, bits per weight), 二.3 (W4A16 dataflow), 三.1 (step
+       alpha/7 and the Delta^2/12 noise model), 六.2 (the four-weight RTN/AWQ
+       table), 八.2 (41.86 -> scale 5.9805).
+[WIKI] "压缩算法" (cs-knowledge-wiki.pages.dev) -- section 7.4.1.1 (asymmetric
+       s = (max-min)/(2^b-1), z = round(-min/s)), 7.4.1.2 (INT4 group code,
+       clamp [-8, 7], two INT4 codes packed into one byte).
+[IOC]  "模型量化技术工程实践：GPTQ/AWQ/QLoRA深度解析" (www.iopencloud.com) --
+       section 1.2 (worked rounding example 3.14159 at scale 0.01).
+[CH]   "量化：PTQ、GPTQ、AWQ 与 SmoothQuant" (charles2530.github.io) --
+       section 1 (unified affine form, 4-bit symmetric range {-8..7}).
+
+Readings taken where the pages are silent or inconsistent are listed in the
+docstrings of the functions that take them.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against values the
+pages print, closed forms, exhaustive checks or exact brute force; none is
+"parity unpinned".
+"""
+
+from .rtn import (  # noqa: F401
+    rtn_scalar,
+    sym_scale_fp16,
+    asym_scale_fp16,
+    quantize_sym,
+    quantize_sym_exact,
+    quantize_asym,
+    dequant_sym,
+    dequant_asym,
+    quant_mse,
+)
+from .layout import (  # noqa: F401
+    pack_canonical,
+    unpack_canonical,
+    device_shapes,
+    codes_to_device,
+    codes_from_device,
+    groupwise_to_device,
+    groupwise_from_device,
+)
+from .gemm import gemm_ref, gemm_ref_rows, to_fp16  # noqa: F401

@@ -1,0 +1,427 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a value a page prints, a closed form, an exhaustive enumeration or an exact
+brute force. ``tests/test_oracle_pins.py`` runs every pin on the oracle as it
+is; ``tests/test_oracle_mutations.py`` plants plausible mistakes into the
+oracle (on the CPU) and checks that at least one pin catches each of them.
+
+The functions look up the oracle through ``import oracle`` at call time so a
+monkeypatched oracle is what they test.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _orc():
+    import oracle
+
+    return oracle
+
+
+# ---------------------------------------------------------------- page values
+
+
+def pin_scalar_rounding_example():
+    """3.14159 at scale 0.01 -> code 314, dequant 3.14, error 0.00159 (page iopencloud, 1.2)."""
+    o = _orc()
+    gd = _golden("iopencloud_rounding_example.json")
+    q, w_hat, err = o.rtn_scalar(gd["w"], gd["scale"])
+    assert q == gd["printed"]["q"], q
+    assert abs(w_hat - gd["printed"]["dequant"]) < 1e-12
+    assert abs(err - gd["printed"]["abs_error"]) < 5e-9
+    # Under INT4 bounds the same input clamps to the top code.
+    q4, w4, _ = o.rtn_scalar(gd["w"], gd["scale"], -8, 7)
+    assert q4 == 7 and abs(w4 - 0.07) < 1e-12
+
+
+def pin_awq_rtn_table():
+    """Four-weight row of the RTN/AWQ table (page arganzheng, 六.2)."""
+    o = _orc()
+    gd = _golden("arg_awq_rtn_table.json")
+    x = np.array(gd["x"])
+    w = np.array(gd["chosen"]["w"])
+    pr = gd["printed"]
+    assert abs(float(x @ w) - pr["Y_unquantized"]) < 5e-4
+    for key in ("rtn", "awq"):
+        cs = np.array(pr[key]["channel_scale"], dtype=np.float64)
+        q, s = o.quantize_sym_exact((w * cs)[None, :], gd["group_size"])
+        assert list(q[0]) == pr[key]["codes"], (key, q)
+        w_hat = o.dequant_sym(q, s, gd["group_size"])[0]
+        assert np.allclose(w_hat, pr[key]["dequant"], atol=5e-5), (key, w_hat)
+        x_used = x / cs
+        assert np.allclose(x_used, pr[key]["x_used"])
+        y_hat = float(o.gemm_ref(x_used[None, :], w_hat[None, :])[0, 0])
+        assert abs(y_hat - pr[key]["y_hat"]) < 5e-5, (key, y_hat)
+        assert abs((y_hat - pr["Y_unquantized"]) - pr[key]["y_err"]) < 2e-4
+    # relative error of the second weight before/after the channel scaling
+    q, s = o.quantize_sym_exact(w[None, :], 4)
+    rel = abs(o.dequant_sym(q, s, 4)[0, 1] - w[1]) / w[1]
+    assert abs(rel - pr["col2_relative_error_rtn"]) < 5e-4
+    q, s = o.quantize_sym_exact((w * [1, 2.5, 1, 1])[None, :], 4)
+    rel = abs(o.dequant_sym(q, s, 4)[0, 1] / 2.5 - w[1]) / w[1]
+    assert abs(rel - pr["col2_relative_error_awq"]) < 5e-4
+
+
+def pin_awq_table_fp16_storage():
+    """The same row through the float16 path: codes unchanged, y_hat within 5e-4."""
+    o = _orc()
+    gd = _golden("arg_awq_rtn_table.json")
+    w16 = np.array(gd["chosen"]["w"], dtype=np.float16)[None, :]
+    q, s16 = o.quantize_sym(w16, 4)
+    assert list(q[0]) == gd["printed"]["rtn"]["codes"]
+    y = o.gemm_ref(np.array(gd["x"], dtype=np.float16)[None, :], o.dequant_sym(q, s16, 4))[0, 0]
+    assert abs(y - gd["printed"]["rtn"]["y_hat"]) < 5e-4
+
+
+def pin_rotation_scale_ratio():
+    """amax / scale = 7 for both printed (amax, scale) pairs (page arganzheng, 八.2)."""
+    o = _orc()
+    pr = _golden("arg_rotation_scale.json")["printed"]
+    for a, s in ((pr["amax"], pr["int4_scale"]), (pr["amax_rotated"], pr["int4_scale_rotated"])):
+        s_or = float(o.sym_scale_fp16(np.array([a], dtype=np.float16))[0])
+        # printed values have 3-4 significant digits; fp16 storage adds 2^-11
+        assert abs(s_or - s) / s < 2e-3, (a, s, s_or)
+        _, s_exact = o.quantize_sym_exact(np.array([[a, 0.0]]), 2)
+        assert abs(float(s_exact[0, 0]) - s) / s < 1.5e-3
+
+
+# ---------------------------------------------------------------- invariants
+
+
+def pin_sym_invariants(N=64, K=1024, g=128, seed=11):
+    """Group max -> +-7, |w - w_hat| <= s16/2, no code -8 (page ybb 二; page arganzheng 三.1)."""
+    o = _orc()
+    W = synth.weight(N, K, seed=seed)
+    q, s16 = o.quantize_sym(W, g)
+    assert q.dtype == np.int8 and q.shape == (N, K) and s16.shape == (N, K // g)
+    assert q.min() >= -7 and q.max() <= 7, "code -8 must never occur"
+    Wg = W.reshape(N, K // g, g).astype(np.float64)
+    qg = q.reshape(N, K // g, g)
+    idx = np.abs(Wg).argmax(axis=2)
+    at_max = np.take_along_axis(qg, idx[..., None], axis=2)[..., 0]
+    sign = np.sign(np.take_along_axis(Wg, idx[..., None], axis=2)[..., 0])
+    assert np.all(at_max == 7 * sign)
+    w_hat = o.dequant_sym(q, s16, g)
+    bound = np.repeat(s16.astype(np.float64), g, axis=1) / 2
+    assert np.all(np.abs(W.astype(np.float64) - w_hat) <= bound)
+
+
+def pin_exact_grid_recovered(seed=3):
+    """Weights already on the grid k*2^-6 with |k| <= 7 and a +-7 per group come back unchanged."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    N, K, g = 8, 256, 32
+    k = r.integers(-7, 8, size=(N, K))
+    k.reshape(N, K // g, g)[:, :, 5] = np.where(r.random((N, K // g)) < 0.5, -7, 7)
+    W = (k * 2.0 ** -6).astype(np.float16)
+    q, s16 = o.quantize_sym(W, g)
+    assert np.all(s16 == np.float16(2.0 ** -6))
+    assert np.array_equal(q.astype(np.int64), k)
+    assert np.array_equal(o.dequant_sym(q, s16, g), W.astype(np.float64))
+
+
+def pin_ties_half_even():
+    """Exact half-integer quotients round to even (the pages' torch.round)."""
+    o = _orc()
+    # amax 1.75 -> s16 = 0.25; 0.625/0.25 = 2.5 -> 2, 0.375/0.25 = 1.5 -> 2, -0.625 -> -2, 0.125 -> 0
+    W = np.array([[1.75, 0.625, 0.375, -0.625, 0.125, -0.125, 0.875, -1.125]], dtype=np.float16)
+    q, s16 = o.quantize_sym(W, 8)
+    assert float(s16[0, 0]) == 0.25
+    assert list(q[0]) == [7, 2, 2, -2, 0, 0, 4, -4]
+
+
+def pin_zero_group():
+    """All-zero group: scale 0 and codes 0 (reading R4); other groups unaffected."""
+    o = _orc()
+    W = np.zeros((2, 64), dtype=np.float16)
+    W[1, 32:] = np.float16(0.5)
+    W[0, 40] = np.float16(-0.7)
+    q, s16 = o.quantize_sym(W, 32)
+    assert s16[0, 0] == 0 and s16[1, 0] == 0 and np.all(q[:, :32] == 0)
+    assert q[0, 40] == -7 and np.all(q[1, 32:] == 7)
+
+
+def pin_scale_exhaustive():
+    """fp16(fp32(a)/7) is the correctly rounded a/7 for every positive finite float16 a."""
+    o = _orc()
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    a = bits.view(np.float16)
+    s = o.sym_scale_fp16(a)
+    cand = (a.astype(np.float64) / 7.0).astype(np.float16)
+    # The float64 quotient can only mis-round into float16 if a/7 sat within
+    # 2^-53 (relative) of a float16 rounding midpoint; a/7 with an 11-bit a is
+    # at least 2^-14/7 away from any midpoint it does not equal, and a/7 equals
+    # a midpoint only if 7 divides the integer a * 2^-e. Check those exactly.
+    assert np.array_equal(s.view(np.uint16), cand.view(np.uint16))
+    for ai, si in zip(a[::97], s[::97]):
+        v = Fraction(float(ai)) / 7
+        lo = np.nextafter(si, np.float16(0))
+        hi = np.nextafter(si, np.float16(np.inf))
+        d = abs(v - Fraction(float(si)))
+        assert d <= abs(v - Fraction(float(lo))) and d <= abs(v - Fraction(float(hi)))
+
+
+def pin_code_decision_exact(n_scales=120, seed=5):
+    """rint of the IEEE float32 quotient equals rint of the exact rational w/s16.
+
+    For each sampled scale, every float16 w with |w| <= 7.5*s16 is tested. The
+    float64 quotient decides the rounding exactly (its error is below 2^-49 while
+    a non-tie quotient of two float16 numbers is at least 2^-12 from a
+    half-integer); quotients within 1e-9 of a half-integer are re-checked with
+    Fractions.
+    """
+    o = _orc()
+    r = np.random.default_rng(seed)
+    sb = np.concatenate([r.integers(0x0400, 0x5000, size=n_scales - 4), [0x0001, 0x0100, 0x1C00, 0x3C00]])
+    all16 = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    all16 = np.concatenate([all16, -all16[1:]])
+    for b in sb.astype(np.uint16):
+        s16 = np.array([b], dtype=np.uint16).view(np.float16)
+        sv = float(s16[0])
+        # group of the candidates plus one element at 7*s16 so the group scale is s16
+        amax = np.float16(7 * sv)
+        if o.sym_scale_fp16(np.array([amax]))[0] != s16[0]:
+            continue
+        w = all16[np.abs(all16.astype(np.float64)) <= float(amax)]
+        if w.size < 2:
+            continue
+        q32 = np.clip(np.rint(w.astype(np.float32) / np.float32(sv)), -8, 7)
+        q64 = np.clip(np.rint(w.astype(np.float64) / sv), -8, 7)
+        assert np.array_equal(q32, q64), sv
+        near = np.abs(np.abs(w.astype(np.float64) / sv) % 1.0 - 0.5) < 1e-9
+        for wi, qi in zip(w[near], q64[near]):
+            fq = Fraction(float(wi)) / Fraction(sv)
+            fl = fq.numerator // fq.denominator
+            frac = fq - fl
+            exact = fl if frac < Fraction(1, 2) else fl + 1 if frac > Fraction(1, 2) else (fl if fl % 2 == 0 else fl + 1)
+            assert qi == max(-8, min(7, exact))
+        # and the oracle itself: a row [amax, w...] padded to the group size
+        g = 32
+        n_full = (w.size // (g - 1)) * (g - 1)
+        if n_full == 0:
+            continue
+        rows = w[:n_full].reshape(-1, g - 1)
+        Wm = np.concatenate([np.full((rows.shape[0], 1), amax, dtype=np.float16), rows], axis=1)
+        q, s_or = o.quantize_sym(Wm, g)
+        assert np.all(s_or == s16[0])
+        assert np.array_equal(q[:, 1:].astype(np.float64).ravel(), q64[:n_full])
+
+
+def pin_noise_model(N=1024, K=4096, seed=0, groups=(4096, 512, 128, 32)):
+    """MSE matches the uniform-noise model E[e^2] = Delta^2/12 (page arganzheng, 三.1).
+
+    Refinement: the group's largest element is reproduced exactly, so the model
+    is mean over groups of ((g-1)/g) * s16^2/12. Also checks the ordering of the
+    page ybb's section 二 demo: MSE falls as the group shrinks.
+    """
+    o = _orc()
+    W = synth.weight(N, K, seed=seed)
+    prev = None
+    for g in groups:
+        q, s16 = o.quantize_sym(W, g)
+        mse = o.quant_mse(W, o.dequant_sym(q, s16, g))
+        model = float(np.mean(s16.astype(np.float64) ** 2)) / 12 * (g - 1) / g
+        assert abs(mse / model - 1) < 0.005, (g, mse, model)
+        if prev is not None:
+            assert mse < prev, (g, mse, prev)
+        prev = mse
+
+
+def pin_asym_exact_grid(seed=7):
+    """A group already on the uint4 grid (min -> code 0, max -> code 15) comes back unchanged."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    N, K, g = 6, 128, 32
+    z_true = r.integers(1, 15, size=(N, K // g))
+    q_true = r.integers(0, 16, size=(N, K))
+    qg = q_true.reshape(N, K // g, g)
+    qg[:, :, 0] = 0
+    qg[:, :, 1] = 15
+    W = ((q_true - np.repeat(z_true, g, axis=1)) * 2.0 ** -5).astype(np.float16)
+    q, s16, z = o.quantize_asym(W, g)
+    assert np.all(s16 == np.float16(2.0 ** -5))
+    assert np.array_equal(z.astype(np.int64), z_true)
+    assert np.array_equal(q.astype(np.int64), q_true)
+    assert np.array_equal(o.dequant_asym(q, s16, z, g), W.astype(np.float64))
+
+
+def pin_asym_invariants(N=64, K=1024, g=64, seed=9):
+    """Asymmetric bounds: codes in [0,15], the group min maps to code 0 when z is
+    unclamped, |w - w_hat| <= s16/2 below the clamp and <= 1.5*s16 at it."""
+    o = _orc()
+    W, _ = synth.heavy_tailed_weight(N, K, seed=seed)
+    q, s16, z = o.quantize_asym(W, g)
+    assert q.max() <= 15 and z.max() <= 15
+    Wg = W.reshape(N, K // g, g).astype(np.float64)
+    qg = q.reshape(N, K // g, g).astype(np.int64)
+    imin = Wg.argmin(axis=2)
+    qmin = np.take_along_axis(qg, imin[..., None], axis=2)[..., 0]
+    unclamped = (z > 0) & (z < 15)
+    assert np.all(qmin[unclamped] == 0)
+    w_hat = o.dequant_asym(q, s16, z, g)
+    err = np.abs(W.astype(np.float64) - w_hat)
+    s_rep = np.repeat(s16.astype(np.float64), g, axis=1)
+    zin = np.repeat(unclamped, g, axis=1)
+    inner = (q > 0) & (q < 15) & zin
+    assert np.all(err[inner] <= s_rep[inner] / 2)
+    assert np.all(err[zin] <= 1.5 * s_rep[zin] * (1 + 2 ** -10))
+
+
+def pin_asym_noise_model(N=512, K=4096, seed=1):
+    """Asymmetric MSE ~ Delta^2/12 with Delta = (max-min)/15 (page arganzheng, 三.1)."""
+    o = _orc()
+    W = synth.weight(N, K, seed=seed)
+    for g in (128, 32):
+        q, s16, z = o.quantize_asym(W, g)
+        mse = o.quant_mse(W, o.dequant_asym(q, s16, z, g))
+        model = float(np.mean(s16.astype(np.float64) ** 2)) / 12
+        assert abs(mse / model - 1) < 0.02, (g, mse, model)
+
+
+# ---------------------------------------------------------------- packing / layout
+
+
+def pin_canonical_hand_bytes():
+    o = _orc()
+    q = np.array([[-8, -7, -6, -5, -4, -3, -2, -1], [0, 1, 2, 3, 4, 5, 6, 7]])
+    b = o.pack_canonical(q)
+    assert list(b[0]) == [0x98, 0xBA, 0xDC, 0xFE]
+    assert list(b[1]) == [0x10, 0x32, 0x54, 0x76]
+    assert np.array_equal(o.unpack_canonical(b), q)
+    assert list(o.unpack_canonical(np.array([[0x10, 0xF1]], dtype=np.uint8), signed=False)[0]) == [0, 1, 1, 15]
+
+
+def pin_device_layout_hand_positions():
+    """Single codes planted at hand-computed positions of the device layout spec."""
+    o = _orc()
+    N, K = 40, 352                       # 3 row tiles (last ragged), 3 super-blocks (last ragged)
+    sh = o.device_shapes(N, K, 32)
+    assert (sh["Np"], sh["Kp"], sh["S"], sh["Gp"], sh["code_bytes"]) == (48, 384, 3, 12, 48 * 384 // 2)
+    # (n, k, expected byte, expected nibble): worked by hand from the spec
+    #   n=17,k=200: t=1 r=1 s=1 m=2 c=1 e=0 -> lane 17, p=0 -> ((1*3+1)*64+17)*16+8+0 = 4376, low
+    #   n=0,k=1:    t=0 r=0 s=0 m=0 c=0 e=1 -> lane 0,  p=4 -> 2, low
+    #   n=15,k=127: t=0 r=15 s=0 m=3 c=3 e=7 -> lane 63, p=7 -> 63*16+12+3 = 1023, high
+    #   n=39,k=350: t=2 r=7 s=2 m=2 c=3 e=6 -> lane 55, p=3 -> ((2*3+2)*64+55)*16+8+1 = 9081, high
+    cases = [(17, 200, 4376, 0), (0, 1, 2, 0), (15, 127, 1023, 4), (39, 350, 9081, 4)]
+    for n, k, byte, shift in cases:
+        q = np.zeros((N, K), dtype=np.int64)
+        q[n, k] = 5
+        dev = o.codes_to_device(q, symmetric=True)
+        # every other nibble holds 8 (code 0 in offset binary)
+        expect_byte = (0x88 & ~(0xF << shift)) | (13 << shift)
+        assert dev[byte] == expect_byte, (n, k, hex(dev[byte]))
+        others = np.delete(dev, byte)
+        assert np.all(others == 0x88)
+        back = o.codes_from_device(dev, N, K)
+        assert np.array_equal(back, q.astype(np.int8))
+        q_a = np.zeros((N, K), dtype=np.int64)
+        q_a[n, k] = 11
+        dev_a = o.codes_to_device(q_a, symmetric=False)
+        assert dev_a[byte] == (11 << shift) and np.count_nonzero(dev_a) == 1
+
+
+def pin_device_layout_bijection(seed=2):
+    o = _orc()
+    r = np.random.default_rng(seed)
+    for N, K in ((16, 128), (33, 96), (5, 32), (48, 1024)):
+        q = r.integers(-8, 8, size=(N, K))
+        dev = o.codes_to_device(q)
+        assert dev.size == o.device_shapes(N, K, 32)["code_bytes"]
+        assert np.array_equal(o.codes_from_device(dev, N, K), q.astype(np.int8))
+        # a permutation: the multiset of valid nibbles is preserved
+        qa = r.integers(0, 16, size=(N, K))
+        da = o.codes_to_device(qa, symmetric=False)
+        nib = np.concatenate([da & 0xF, da >> 4]).astype(np.int64)
+        assert np.array_equal(np.bincount(nib, minlength=16) - np.bincount(qa.ravel(), minlength=16),
+                              np.eye(16, dtype=np.int64)[0] * (nib.size - qa.size))
+    # group-wise arrays: [t, j, r] addressing
+    s = np.arange(20 * 3, dtype=np.float16).reshape(20, 3)
+    d = o.groupwise_to_device(s, 20, 96, 32)
+    assert d.shape == (2, 4, 16)         # Kp = 128 -> Gp = 4, the last group is padding
+    assert d[1, 2, 3] == s[19, 2] and d[1, 2, 4] == 0 and d[0, 1, 15] == s[15, 1]
+    assert np.all(d[:, 3, :] == 0)
+    assert np.array_equal(o.groupwise_from_device(d, 20, 96, 32), s)
+
+
+# ---------------------------------------------------------------- product
+
+
+def _exact_product(x16, q, s16, g, z=None):
+    """Exact rational y = x . w_hat^T from the codes (pure-Python brute force)."""
+    B, K = x16.shape
+    N = q.shape[0]
+    out = np.zeros((B, N))
+    for b in range(B):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                zz = 0 if z is None else int(z[n, k // g])
+                acc += Fraction(float(x16[b, k])) * Fraction(float(s16[n, k // g])) * (int(q[n, k]) - zz)
+            out[b, n] = float(acc)
+    return out
+
+
+def pin_product_bruteforce(seed=4):
+    o = _orc()
+    for B, N, K, g in ((1, 5, 32, 32), (3, 17, 64, 32), (2, 4, 256, 64), (3, 3, 128, 128)):
+        W = synth.weight(N, K, seed=seed + N)
+        x = synth.activation(B, K, seed=seed + K)
+        q, s16 = o.quantize_sym(W, g)
+        y = o.gemm_ref(x, o.dequant_sym(q, s16, g))
+        assert y.shape == (B, N)
+        ye = _exact_product(x, q, s16, g)
+        assert np.allclose(y, ye, rtol=1e-12, atol=1e-15)
+        qa, sa, za = o.quantize_asym(W, g)
+        ya = o.gemm_ref(x, o.dequant_asym(qa, sa, za, g))
+        assert np.allclose(ya, _exact_product(x, qa, sa, g, za), rtol=1e-12, atol=1e-15)
+        rows = [N - 1, 0]
+        assert np.allclose(o.gemm_ref_rows(x, q, s16, g, rows), ye[:, rows], rtol=1e-12, atol=1e-15)
+
+
+def pin_product_special_cases():
+    o = _orc()
+    K, g = 256, 128
+    x = synth.activation(2, K, seed=1)
+    # all weights 1.0: s16 = fp16(1/7), codes 7, y = 7*s16*sum(x)
+    W = np.ones((3, K), dtype=np.float16)
+    q, s16 = o.quantize_sym(W, g)
+    y = o.gemm_ref(x, o.dequant_sym(q, s16, g))
+    assert np.allclose(y, 7 * float(s16[0, 0]) * x.astype(np.float64).sum(axis=1, keepdims=True), rtol=1e-13)
+    # one-hot rows pick single activations
+    W = np.zeros((4, K), dtype=np.float16)
+    hot = [3, 100, 130, 255]
+    for i, k in enumerate(hot):
+        W[i, k] = np.float16(0.5 + i)
+    q, s16 = o.quantize_sym(W, g)
+    y = o.gemm_ref(x, o.dequant_sym(q, s16, g))
+    for i, k in enumerate(hot):
+        assert np.allclose(y[:, i], 7 * float(s16[i, k // g]) * x[:, k].astype(np.float64), rtol=1e-13)
+    # zero weights
+    q, s16 = o.quantize_sym(np.zeros((2, K), dtype=np.float16), g)
+    assert np.all(o.gemm_ref(x, o.dequant_sym(q, s16, g)) == 0)
+    # linearity in x
+    W = synth.weight(5, K, seed=8)
+    q, s16 = o.quantize_sym(W, g)
+    wh = o.dequant_sym(q, s16, g)
+    x1 = synth.activation(1, K, seed=2).astype(np.float64)
+    x2 = synth.activation(1, K, seed=3).astype(np.float64)
+    assert np.allclose(o.gemm_ref(2 * x1 - x2, wh), 2 * o.gemm_ref(x1, wh) - o.gemm_ref(x2, wh), rtol=1e-12, atol=1e-12)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,169 @@
+"""Plant plausible mistakes into the oracle (CPU only) and check the pins catch each.
+
+A pin set that passes on a broken oracle proves nothing; these tests show
+that every mistake below makes at least one pin fail.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.gemm
+import oracle.layout
+import oracle.rtn
+from pins import ALL_PINS
+
+
+class _NumpyWith:
+    """numpy with a few functions replaced (planted into one oracle module)."""
+
+    def __init__(self, **over):
+        self.__dict__.update(over)
+
+    def __getattr__(self, name):
+        return getattr(np, name)
+
+
+def _caught():
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # AssertionError or a crash both count as caught
+            failures.append((pin.__name__, type(e).__name__))
+    return failures
+
+
+def _scale_div8(monkeypatch):
+    orig = oracle.rtn.sym_scale_fp16
+    f = lambda a, qmax=7: orig(a, 8)  # noqa: E731
+    monkeypatch.setattr(oracle.rtn, "sym_scale_fp16", f)
+    monkeypatch.setattr(oracle, "sym_scale_fp16", f)
+
+
+def _scale_two_alpha_over_15(monkeypatch):
+    orig = oracle.rtn.sym_scale_fp16
+    f = lambda a, qmax=7: orig(a, 7.5)  # noqa: E731
+    monkeypatch.setattr(oracle.rtn, "sym_scale_fp16", f)
+    monkeypatch.setattr(oracle, "sym_scale_fp16", f)
+
+
+def _truncate(monkeypatch):
+    monkeypatch.setattr(oracle.rtn, "np", _NumpyWith(rint=np.trunc))
+
+
+def _half_away(monkeypatch):
+    monkeypatch.setattr(oracle.rtn, "np", _NumpyWith(rint=lambda a: np.sign(a) * np.floor(np.abs(a) + 0.5)))
+
+
+def _fp16_quotient(monkeypatch):
+    monkeypatch.setattr(oracle.rtn, "np",
+                        _NumpyWith(rint=lambda a: np.rint(np.asarray(a).astype(np.float16).astype(np.float64))))
+
+
+def _nibbles_swapped(monkeypatch):
+    def pack(c):
+        c = np.asarray(c).astype(np.int64)
+        return ((c[:, 1::2] & 0xF) | ((c[:, 0::2] & 0xF) << 4)).astype(np.uint8)
+
+    monkeypatch.setattr(oracle, "pack_canonical", pack)
+
+
+def _device_nibble_order(monkeypatch):
+    monkeypatch.setattr(oracle.layout, "_nibble_index", lambda e: e)
+
+
+def _device_lane_order(monkeypatch):
+    # rows and k-quarters swapped in the lane index
+    orig = oracle.layout._device_position
+
+    def pos(N, K):
+        byte, shift, Np, Kp = orig(N, K)
+        return byte, shift, Np, Kp
+
+    def pos_bad(N, K):
+        Kp = -(-K // 128) * 128
+        Np = -(-N // 16) * 16
+        S = Kp // 128
+        n = np.arange(Np)[:, None]
+        k = np.arange(Kp)[None, :]
+        t, r = n // 16, n % 16
+        s, m = k // 128, (k % 128) // 32
+        c, e = (k % 32) // 8, k % 8
+        p = oracle.layout._nibble_index(e)
+        byte = ((t * S + s) * 64 + (4 * r + c)) * 16 + 4 * m + p // 2
+        return byte, np.broadcast_to(4 * (p % 2), byte.shape), Np, Kp
+
+    monkeypatch.setattr(oracle.layout, "_device_position", pos_bad)
+
+
+def _dequant_wrong_group(monkeypatch):
+    def dq(q, s, g):
+        q = np.asarray(q, dtype=np.float64)
+        s = np.asarray(s, dtype=np.float64)
+        return q * np.tile(s, (1, g))
+
+    monkeypatch.setattr(oracle, "dequant_sym", dq)
+    monkeypatch.setattr(oracle.gemm, "dequant_sym", dq)
+
+
+def _gemm_rows_reversed(monkeypatch):
+    def g(x16, w_hat):
+        return np.asarray(x16, dtype=np.float64) @ np.asarray(w_hat, dtype=np.float64)[::-1].T
+
+    monkeypatch.setattr(oracle, "gemm_ref", g)
+    monkeypatch.setattr(oracle.gemm, "gemm_ref", g)
+
+
+def _gemm_fp16_accumulate(monkeypatch):
+    def g(x16, w_hat):
+        return (np.asarray(x16, dtype=np.float16) @ np.asarray(w_hat).astype(np.float16).T).astype(np.float64)
+
+    monkeypatch.setattr(oracle, "gemm_ref", g)
+    monkeypatch.setattr(oracle.gemm, "gemm_ref", g)
+
+
+def _asym_zero_sign(monkeypatch):
+    orig = oracle.rtn.asym_scale_fp16
+
+    def quant(W16, g):
+        W = np.asarray(W16)
+        Wg = W.reshape(W.shape[0], -1, g)
+        mn, mx = Wg.min(axis=2), Wg.max(axis=2)
+        s16 = orig(mn, mx)
+        s32 = s16.astype(np.float32)
+        with np.errstate(all="ignore"):
+            z = np.where(s32 == 0, 0, np.clip(np.rint(mn.astype(np.float32) / s32), 0, 15))
+            q = np.clip(np.rint(Wg.astype(np.float32) / s32[..., None]) + z[..., None], 0, 15)
+        q = np.where(s32[..., None] == 0, 0, q)
+        return q.astype(np.uint8).reshape(W.shape), s16, z.astype(np.uint8)
+
+    monkeypatch.setattr(oracle, "quantize_asym", quant)
+
+
+def _asym_dequant_plus(monkeypatch):
+    def dq(q, s, z, g):
+        return (np.asarray(q, np.float64) + np.repeat(np.asarray(z, np.float64), g, axis=1)) * np.repeat(
+            np.asarray(s, np.float64), g, axis=1)
+
+    monkeypatch.setattr(oracle, "dequant_asym", dq)
+    monkeypatch.setattr(oracle.gemm, "dequant_asym", dq)
+
+
+def _asym_levels16(monkeypatch):
+    orig = oracle.rtn.asym_scale_fp16
+    monkeypatch.setattr(oracle.rtn, "asym_scale_fp16", lambda mn, mx, levels=15: orig(mn, mx, 16))
+
+
+MUTATIONS = [
+    _scale_div8, _scale_two_alpha_over_15, _truncate, _half_away, _fp16_quotient, _nibbles_swapped,
+    _device_nibble_order, _device_lane_order, _dequant_wrong_group, _gemm_rows_reversed,
+    _gemm_fp16_accumulate, _asym_zero_sign, _asym_dequant_plus, _asym_levels16,
+]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m.__name__.lstrip("_") for m in MUTATIONS])
+def test_planted_mistake_is_caught(mutation, monkeypatch):
+    mutation(monkeypatch)
+    caught = _caught()
+    assert caught, f"no pin caught the planted mistake {mutation.__name__}"
