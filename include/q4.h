@@ -1,0 +1,163 @@
+/*
+ * q4.h -- C ABI of libq4: group-wise INT4 round-to-nearest weight quantization
+ * and the fused dequantize-and-multiply W4A16 product, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources of the method (cited by page title and section):
+ *  [YBB]  "LLM 后训练量化深度实战：从 GPTQ/AWQ 到 FP8 与 KV Cache 量化的显存-带宽极限工程"
+ *         (www.ybb.press), section 二: quantize_per_group (scale = group amax / 7,
+ *         codes rounded and clamped to [-8, 7], one scale per group of input
+ *         channels, in_features must be a multiple of the group size); section 一:
+ *         the decode GEMV y = x W^T is bound by the bytes of W it reads.
+ *  [ARG]  "Post-training quantization: GPTQ, AWQ and rotation" (arganzheng.life),
+ *         section 二.2: affine form q = clamp(round(w/s) + z, 0, 2^b - 1),
+ *         w_hat = s (q - z), asymmetric s = (max - min)/(2^b - 1), integer z;
+ *         per-group scales must be applied inside the k-accumulation; bits per
+ *         weight. Section 二.3: W4A16 reads INT4 weights, dequantizes them on chip
+ *         and multiplies with 16-bit activations; the FLOPs are unchanged.
+ *  [WIKI] "压缩算法" (cs-knowledge-wiki.pages.dev), section 7.4.1.1: z = round(-min/s);
+ *         section 7.4.1.2: INT4 codes in [-8, 7], two codes packed per byte.
+ *  [CH]   "量化：PTQ、GPTQ、AWQ 与 SmoothQuant" (charles2530.github.io), section 1:
+ *         4-bit symmetric range {-8, ..., 7}.
+ *
+ * Conventions common to every call
+ *  - Matrices are row-major. W is [out][in] float16 (a linear layer's weight,
+ *    y = x W^T); x is [B][in] float16; y is [B][out] float16.
+ *  - All pointers except `stream` are DEVICE pointers owned by the caller. The
+ *    library never allocates, frees or caches device memory and keeps no global
+ *    state: calls are thread-safe and re-entrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *    work on it and never synchronize.
+ *  - Arguments are validated on the host before any HIP call; a failed check
+ *    returns its status and enqueues nothing. A HIP launch error returns
+ *    Q4_ERR_HIP. q4_last_error() describes the most recent failure on the
+ *    calling thread.
+ *  - Supported group sizes g: 32, 64 and every multiple of 128. `in` must be a
+ *    positive multiple of g. `out` >= 1; `B` >= 0 (B = 0 enqueues nothing).
+ *    out and in must each be below 2^30.
+ *  - Non-finite weights give unspecified codes and scales (no scan is made).
+ *
+ * Device layout of the packed codes (opaque to callers; q4_to_canonical and
+ * q4_from_canonical convert). With Np = ceil(out/16)*16, Kp = ceil(in/128)*128
+ * and S = Kp/128, code (n, k) with t = n/16, r = n%16, s = k/128,
+ * m = (k%128)/32, c = (k%32)/8, e = k%8 is the nibble p(e)%2 (0 = low) of byte
+ *     ((t*S + s)*64 + r + 16*c)*16 + 4*m + p(e)/2,   p(e) = e/2 (e even), 4 + (e-1)/2 (e odd).
+ * Symmetric codes are stored offset-binary (q + 8), asymmetric codes as q.
+ * Rows >= out and channels >= in are padding holding code 0. Each 1 KiB block
+ * is one 16-row x 128-channel tile: one 16-byte load per lane of a 64-lane
+ * wavefront, already in the A-operand order of v_mfma_f32_16x16x32_f16.
+ *
+ * Device layout of per-group arrays (float16 scales, uint8 zero points): with
+ * Gp = Kp/g, element (n, j) sits at index (t*Gp + j)*16 + r; padding is 0.
+ *
+ * Canonical layout (what q4_to_canonical returns): codes [out][in/2] bytes,
+ * byte (n, i) = (c[n][2i] & 0xF) | (c[n][2i+1] & 0xF) << 4, symmetric codes in
+ * 4-bit two's complement; scales [out][in/g] float16; zeros [out][in/g] uint8.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  Q4_OK = 0,
+  Q4_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  Q4_ERR_SHAPE = 2,       /* out/in/B out of range or overflowing                        */
+  Q4_ERR_GROUP = 3,       /* group unsupported, or in % group != 0 ([YBB] section 二)    */
+  Q4_ERR_ALIGN = 4,       /* a pointer is not aligned as the call requires               */
+  Q4_ERR_UNSUPPORTED = 5, /* a valid request this build does not handle (e.g. config)    */
+  Q4_ERR_WORKSPACE = 6,   /* workspace smaller than q4_workspace_bytes() asks for        */
+  Q4_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                  */
+} q4_status;
+
+/* Static English description of a status code. Never NULL. */
+const char* q4_status_str(int status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* q4_last_error(void);
+
+/* Library version string, e.g. "q4 1.0.0 gfx950". */
+const char* q4_version(void);
+
+/* 1 if `group` is a supported group size, else 0. */
+int32_t q4_group_supported(int32_t group);
+
+/* Bytes of the device-layout packed code buffer for an [out][in] matrix:
+ * ceil(out/16)*16 * ceil(in/128)*128 / 2. 0 if out or in is not positive. */
+size_t q4_packed_bytes(int64_t out, int64_t in);
+
+/* Elements of a device-layout per-group array (scales or zeros):
+ * ceil(out/16)*16 * ceil(in/128)*128/group. 0 on invalid arguments. */
+size_t q4_groups_count(int64_t out, int64_t in, int32_t group);
+
+/* Symmetric quantize + pack ([YBB] section 二; [WIKI] section 7.4.1.2):
+ *   s16[n][j] = float16_rne(float32(max_{k in group j} |W[n][k]|) / 7.0f)
+ *   q[n][k]   = clamp(rint_half_even(float32(W[n][k]) / float32(s16)), -8, 7),
+ *               q = 0 wherever s16 == 0 (an all-zero or underflowing group).
+ * IEEE float32 division. Writes q4_packed_bytes(out, in) bytes to `packed`
+ * (16-byte aligned) and q4_groups_count(out, in, group) float16 to `scales`
+ * (8-byte aligned), both in device layout, padding included. W: [out][in]
+ * float16, 16-byte aligned. */
+q4_status q4_quantize_pack(const void* W, int64_t out, int64_t in, int32_t group,
+                           void* packed, void* scales, void* stream);
+
+/* Asymmetric uint4 quantize + pack ([ARG] section 二.2; [WIKI] section 7.4.1.1):
+ *   s16 = float16_rne(float32(float32(max) - float32(min)) / 15.0f)
+ *   z   = clamp(rint(-min / s16), 0, 15),  q = clamp(rint(w / s16) + z, 0, 15),
+ *   q = z = 0 wherever s16 == 0.  w_hat = s16 * (q - z).
+ * As q4_quantize_pack, plus q4_groups_count() uint8 zero points in `zeros`. */
+q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t group,
+                                void* packed, void* scales, void* zeros, void* stream);
+
+/* Bytes of workspace q4_gemm needs for this shape (0 in this version: the
+ * k-split is reduced inside each workgroup, no scratch memory is used). */
+size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group);
+
+/* Fused W4A16 product ([ARG] sections 二.2 and 二.3; [YBB] section 一):
+ *   y[b][n] = float16_rne( sum_j s16[n][j] * sum_{k in group j} x[b][k] * q[n][k] )
+ * with float16 x and codes, float32 accumulation, the group scale applied to
+ * each group's partial sum inside the k-loop. Any B >= 0: B <= 16 runs the
+ * GEMV kernel (one 16-column MFMA tile, padded), larger B the skinny-GEMM
+ * tiling. x: [B][in] float16, 16-byte aligned; packed/scales as written by
+ * q4_quantize_pack; y: [B][out] float16, 2-byte aligned.
+ * `workspace` may be NULL when q4_workspace_bytes() returns 0. */
+q4_status q4_gemm(const void* x, int64_t B, const void* packed, const void* scales,
+                  int64_t out, int64_t in, int32_t group, void* y,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* As q4_gemm for asymmetric weights: the inner sum uses (q - z[n][j]). */
+q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void* scales,
+                       const void* zeros, int64_t out, int64_t in, int32_t group, void* y,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* q4_gemm with an explicit launch shape, for tuning: `rows_per_wave` row tiles
+ * of 16 per wavefront (1, 2 or 4), `waves_per_group` wavefronts per workgroup
+ * (1..16) splitting the in dimension. Returns Q4_ERR_UNSUPPORTED for shapes
+ * outside those ranges. `asym` selects q4_gemm_asym semantics (zeros used). */
+q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales,
+                         const void* zeros, int32_t asym, int64_t out, int64_t in, int32_t group,
+                         void* y, int32_t rows_per_wave, int32_t waves_per_group, void* stream);
+
+/* Device layout -> canonical layout (see above). `zeros`/`canon_zeros` are used
+ * only when asym != 0. canon_codes: out*in/2 bytes; canon_scales: out*(in/group)
+ * float16; canon_zeros: out*(in/group) bytes. */
+q4_status q4_to_canonical(const void* packed, const void* scales, const void* zeros, int32_t asym,
+                          int64_t out, int64_t in, int32_t group,
+                          void* canon_codes, void* canon_scales, void* canon_zeros, void* stream);
+
+/* Canonical layout -> device layout, padding included: imports codes and scales
+ * produced elsewhere (e.g. by another quantizer with the same format). */
+q4_status q4_from_canonical(const void* canon_codes, const void* canon_scales, const void* canon_zeros,
+                            int32_t asym, int64_t out, int64_t in, int32_t group,
+                            void* packed, void* scales, void* zeros, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

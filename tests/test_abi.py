@@ -1,0 +1,133 @@
+"""The C ABI library on the CPU: it loads, exports what include/q4.h declares,
+shares torch's HIP runtime, and rejects bad arguments before any HIP call.
+
+No test here launches a kernel; each invalid call below returns from the
+host-side validation.
+"""
+
+import ctypes
+import json
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from w4a16_decode_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from w4a16_decode_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    from w4a16_decode_amd import _lib
+
+    declared = _lib.header_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in include/q4.h but not exported"
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature in the binding"
+    assert sorted(_lib.SIGNATURES) == declared
+
+
+def test_single_hip_runtime(lib):
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(hip) == 1, hip
+    import torch
+
+    assert os.path.dirname(next(iter(hip))) == os.path.join(os.path.dirname(torch.__file__), "lib")
+
+
+def test_version_and_status_strings(lib):
+    assert lib.q4_version().decode().startswith("q4 ")
+    assert lib.q4_status_str(0) == b"ok"
+    for st in range(1, 8):
+        assert lib.q4_status_str(st) and lib.q4_status_str(st) != b"unknown status"
+    assert lib.q4_status_str(99) == b"unknown status"
+
+
+def test_sizes(lib):
+    assert lib.q4_packed_bytes(4096, 4096) == 4096 * 4096 // 2
+    assert lib.q4_packed_bytes(17, 96) == 32 * 128 // 2          # padded to 16 rows, 128 channels
+    assert lib.q4_packed_bytes(0, 128) == 0
+    assert lib.q4_groups_count(4096, 4096, 128) == 4096 * 32
+    assert lib.q4_groups_count(20, 96, 32) == 32 * 4            # Gp = ceil(96/128)*128/32
+    assert lib.q4_groups_count(20, 96, 64) == 0                  # 96 % 64 != 0
+    assert lib.q4_workspace_bytes(1, 4096, 4096, 128) == 0
+    for g, ok in ((32, 1), (64, 1), (128, 1), (256, 1), (4096, 1), (96, 0), (16, 0), (0, 0), (-128, 0), (192, 0)):
+        assert lib.q4_group_supported(g) == ok, g
+
+
+FAKE = 0x100000  # a 16-byte-aligned non-NULL address that is never dereferenced
+
+
+def test_quantize_validation(lib):
+    f = lib.q4_quantize_pack
+    assert f(None, 16, 128, 128, FAKE, FAKE, None) == 1
+    assert f(FAKE, 16, 128, 128, None, FAKE, None) == 1
+    assert f(FAKE, 0, 128, 128, FAKE, FAKE, None) == 2
+    assert f(FAKE, 16, -128, 128, FAKE, FAKE, None) == 2
+    assert f(FAKE, 1 << 30, 128, 128, FAKE, FAKE, None) == 2
+    assert f(FAKE, 16, 96, 64, FAKE, FAKE, None) == 3            # in % group != 0
+    assert b"multiple" in lib.q4_last_error()
+    assert f(FAKE, 16, 96, 96, FAKE, FAKE, None) == 3            # unsupported group
+    assert f(FAKE + 2, 16, 128, 128, FAKE, FAKE, None) == 4      # W misaligned
+    assert f(FAKE, 16, 128, 128, FAKE + 8, FAKE, None) == 4      # packed misaligned
+    assert f(FAKE, 16, 128, 128, FAKE, FAKE + 2, None) == 4      # scales misaligned
+    assert lib.q4_quantize_pack_asym(FAKE, 16, 128, 128, FAKE, FAKE, None, None) == 1
+
+
+def test_gemm_validation(lib):
+    g = lib.q4_gemm
+    assert g(FAKE, -1, FAKE, FAKE, 16, 128, 128, FAKE, None, 0, None) == 2
+    assert g(None, 0, None, None, 16, 128, 128, None, None, 0, None) == 0      # B = 0: nothing to do
+    assert g(None, 1, FAKE, FAKE, 16, 128, 128, FAKE, None, 0, None) == 1
+    assert g(FAKE, 1, FAKE, FAKE, 16, 100, 32, FAKE, None, 0, None) == 3
+    assert g(FAKE + 4, 1, FAKE, FAKE, 16, 128, 128, FAKE, None, 0, None) == 4
+    assert g(FAKE, 1, FAKE, FAKE, 16, 128, 128, FAKE + 1, None, 0, None) == 4
+    assert lib.q4_gemm_asym(FAKE, 1, FAKE, FAKE, None, 16, 128, 128, FAKE, None, 0, None) == 1
+    c = lib.q4_gemm_config
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 3, 1, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 9, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 0, 0, None) == 5
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 8, None) == 5  # reduction buffer too big
+
+
+def test_layout_validation(lib):
+    assert lib.q4_to_canonical(None, FAKE, None, 0, 16, 128, 128, FAKE, FAKE, None, None) == 1
+    assert lib.q4_to_canonical(FAKE, FAKE, None, 1, 16, 128, 128, FAKE, FAKE, None, None) == 1
+    assert lib.q4_from_canonical(FAKE, FAKE, None, 0, 16, 100, 32, FAKE, FAKE, None, None) == 3
+
+
+def test_bits_per_weight_matches_pages():
+    from w4a16_decode_amd import perfmodel
+
+    gd = json.load(open(os.path.join(ROOT, "tests", "golden", "arg_bits_per_weight.json")))
+    for row in gd["printed"]:
+        got = perfmodel.bits_per_weight(row["g"], 4, row["b_scale"], row["b_zero"])
+        digits = len(str(row["bits"]).split(".")[1])
+        assert abs(got - row["bits"]) <= 0.5 * 10 ** -digits + 1e-12, row
+    for row in gd["printed_bytes"]:
+        digits = len(str(row["GB"]).split(".")[1])
+        assert abs(row["params"] * row["bits"] / 8 / 1e9 - row["GB"]) <= 0.5 * 10 ** -digits + 1e-9, row
+    # our symmetric format: float16 scale, no zero point
+    assert perfmodel.weight_bytes(4096, 4096, 128) == 4096 * 4096 // 2 + 2 * 4096 * 32
+    assert perfmodel.gemm_read_bytes(1, 4096, 4096, 128) == 8_658_944
+
+
+def test_time_model_matches_page_numbers():
+    """T_mem 16.06 GB / 3.35 TB/s ~ 4.8 ms; T_cmp(m) ~ m * 15.2 us; crossover B* ~ 79."""
+    from w4a16_decode_amd import perfmodel
+
+    t = perfmodel.time_model_s(16.06e9, 7.5e9, 1, 3.35e12, 989e12)
+    assert abs(t * 1e3 - 4.8) < 0.05
+    assert abs(perfmodel.time_model_s(0, 7.5e9, 1, 3.35e12, 989e12) * 1e6 - 15.2) < 0.1
+    t_w4 = 4.0e9 / 3.35e12
+    assert abs(t_w4 / (2 * 7.5e9 / 989e12) - 79) < 1.0

@@ -1,0 +1,225 @@
+"""HIP path vs the oracle, through the C ABI (needs an MI355X).
+
+Quantization must match bit for bit (codes, scales, zero points, padding);
+products must meet relative L2 <= 1e-3 and max |dy| <= 1e-3 * max |y|.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_close, say, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL_SHAPES = [  # (N, K, g): several tiles, ragged row and channel tails
+    (1, 32, 32), (17, 96, 32), (33, 192, 64), (40, 352, 32), (48, 384, 128),
+    (31, 512, 256), (16, 4096, 4096), (100, 1280, 128), (129, 640, 64), (64, 2048, 512),
+]
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import w4a16_decode_amd as q4mod
+
+    say("libq4", q4mod.version())
+    return q4mod
+
+
+def _oracle_quant(W, g, asym):
+    if asym:
+        return oracle.quantize_asym(W, g)
+    q, s = oracle.quantize_sym(W, g)
+    return q, s, None
+
+
+def _check_quant_exact(q4, W, g, asym, device_layout=True):
+    N, K = W.shape
+    qw = q4.quantize_pack(to_gpu(W), g, asym=asym)
+    q_o, s_o, z_o = _oracle_quant(W, g, asym)
+    codes, scales, zeros = q4.to_canonical(qw)
+    assert np.array_equal(to_np(codes), oracle.pack_canonical(q_o)), (N, K, g, asym, "canonical codes")
+    assert np.array_equal(to_np(scales).view(np.uint16), s_o.view(np.uint16)), (N, K, g, asym, "scales")
+    if asym:
+        assert np.array_equal(to_np(zeros), z_o), (N, K, g, "zeros")
+    if device_layout:
+        assert np.array_equal(to_np(qw.packed), oracle.codes_to_device(q_o, symmetric=not asym)), "device codes"
+        dev_s = oracle.groupwise_to_device(s_o, N, K, g).ravel()
+        assert np.array_equal(to_np(qw.scales).view(np.uint16), dev_s.view(np.uint16)), "device scales"
+        if asym:
+            assert np.array_equal(to_np(qw.zeros), oracle.groupwise_to_device(z_o, N, K, g).ravel())
+    return qw, q_o, s_o, z_o
+
+
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
+@pytest.mark.parametrize("N,K,g", SMALL_SHAPES)
+def test_quantize_small_bit_exact(q4, N, K, g, asym):
+    say(f"quantize N={N} K={K} g={g} asym={asym}")
+    W = synth.weight(N, K, seed=N * 7 + K)
+    _check_quant_exact(q4, W, g, asym)
+
+
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
+def test_quantize_edge_values(q4, asym):
+    say(f"quantize edge values asym={asym}")
+    N, K = 37, 384
+    cases = {
+        "ties_and_zero_groups": synth.uniform_codes_weight(N, K, seed=1),
+        "all_zero": np.zeros((N, K), dtype=np.float16),
+        "tiny": (synth.weight(N, K, seed=2).astype(np.float32) * np.float32(1e-4)).astype(np.float16),
+        "subnormal": (np.arange(N * K) % 7 - 3).reshape(N, K).astype(np.float16) * np.float16(2.0 ** -24),
+        "huge": (synth.weight(N, K, seed=3).astype(np.float32) * np.float32(2.0e4)).clip(-65504, 65504).astype(np.float16),
+        "constant_rows": np.full((N, K), 0.5, dtype=np.float16),
+        "one_sided": np.abs(synth.weight(N, K, seed=4)) + np.float16(0.01),
+    }
+    for name, W in cases.items():
+        for g in (32, 128):
+            say(f"  {name} g={g}")
+            _check_quant_exact(q4, W, g, asym)
+
+
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_quantize_heavy_tailed_full(q4, g, asym):
+    """The heavy-tailed 14336x4096 workload (Student-t df=3, 1% outlier columns x50)."""
+    say(f"quantize heavy-tailed 14336x4096 g={g} asym={asym}")
+    W, _ = synth.heavy_tailed_weight(14336, 4096, seed=5)
+    _check_quant_exact(q4, W, g, asym, device_layout=False)
+
+
+def test_quantize_single_layer_full(q4):
+    """4096x4096, N(0, 0.02^2), g=128, seed 0: codes and scales bit-exact, layout included."""
+    say("quantize 4096x4096 g=128")
+    W = synth.weight(4096, 4096, seed=0)
+    _check_quant_exact(q4, W, 128, False)
+
+
+def test_canonical_round_trip(q4):
+    for N, K, g, asym in ((40, 352, 32, False), (33, 192, 64, True), (100, 1280, 128, True)):
+        W = synth.weight(N, K, seed=9)
+        q_o, s_o, z_o = _oracle_quant(W, g, asym)
+        qw = q4.from_canonical(to_gpu(oracle.pack_canonical(q_o)), to_gpu(s_o), g,
+                               zeros=to_gpu(z_o) if asym else None)
+        assert np.array_equal(to_np(qw.packed), oracle.codes_to_device(q_o, symmetric=not asym))
+        assert np.array_equal(to_np(qw.scales).view(np.uint16),
+                              oracle.groupwise_to_device(s_o, N, K, g).ravel().view(np.uint16))
+        c, s, z = q4.to_canonical(qw)
+        assert np.array_equal(to_np(c), oracle.pack_canonical(q_o))
+
+
+def _ref_product(x, q_o, s_o, z_o, g):
+    w_hat = oracle.dequant_asym(q_o, s_o, z_o, g) if z_o is not None else oracle.dequant_sym(q_o, s_o, g)
+    return oracle.gemm_ref(x, w_hat)
+
+
+GEMM_CASES = [  # (B, N, K, g, asym)
+    (1, 1, 32, 32, False), (1, 17, 96, 32, False), (3, 40, 352, 32, True), (2, 33, 192, 64, False),
+    (4, 48, 384, 128, True), (5, 31, 512, 256, False), (7, 100, 1280, 128, False), (8, 129, 640, 64, True),
+    (9, 64, 2048, 128, False), (15, 47, 1024, 128, False), (16, 200, 1024, 128, True), (17, 100, 512, 128, False),
+    (31, 48, 1024, 64, False), (33, 65, 768, 128, True), (64, 128, 2048, 128, False), (65, 40, 512, 32, False),
+    (100, 300, 1024, 128, False), (256, 96, 1024, 128, True), (1, 16, 4096, 4096, False), (2, 4000, 256, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,N,K,g,asym", GEMM_CASES)
+def test_gemm_small(q4, B, N, K, g, asym):
+    say(f"gemm B={B} N={N} K={K} g={g} asym={asym}")
+    W = synth.weight(N, K, seed=B + N)
+    x = synth.activation(B, K, seed=K + B)
+    qw, q_o, s_o, z_o = _check_quant_exact(q4, W, g, asym, device_layout=False)
+    y = q4.gemm(to_gpu(x), qw)
+    assert_close(to_np(y), _ref_product(x, q_o, s_o, z_o, g), f"B={B} N={N} K={K} g={g}")
+
+
+def test_gemm_launch_shapes_agree(q4):
+    """Every tuning shape of the same kernel meets the tolerance; each is deterministic."""
+    B, N, K, g = 4, 300, 2048, 128
+    W = synth.weight(N, K, seed=1)
+    x = synth.activation(B, K, seed=2)
+    qw, q_o, s_o, _ = _check_quant_exact(q4, W, g, False, device_layout=False)
+    ref = _ref_product(x, q_o, s_o, None, g)
+    xg = to_gpu(x)
+    for R in (1, 2, 4):
+        for Wv in (1, 2, 4, 8):
+            say(f"  config R={R} W={Wv}")
+            y1 = to_np(q4.gemm_config(xg, qw, R, Wv))
+            y2 = to_np(q4.gemm_config(xg, qw, R, Wv))
+            assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "non-deterministic"
+            assert_close(y1, ref, f"R={R} W={Wv}")
+
+
+def test_gemm_empty_batch(q4):
+    import torch
+
+    qw = q4.quantize_pack(to_gpu(synth.weight(32, 128)), 128)
+    y = q4.gemm(torch.empty((0, 128), dtype=torch.float16, device="cuda"), qw)
+    assert tuple(y.shape) == (0, 32)
+
+
+def _sampled_rows(N, n, seed):
+    r = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, N - 1], r.choice(N, size=min(n, N), replace=False)]))
+    return rows
+
+
+def _full_size_check(q4, N, K, g, Bs, asym=False, seed=0, heavy=False, nrows=96):
+    import torch
+
+    W = synth.heavy_tailed_weight(N, K, seed=seed)[0] if heavy else synth.weight(N, K, seed=seed)
+    Wg = to_gpu(W)
+    qw = q4.quantize_pack(Wg, g, asym=asym)
+    del Wg
+    rows = _sampled_rows(N, nrows, seed + 1)
+    if asym:
+        q_o, s_o, z_o = oracle.quantize_asym(W[rows], g)
+    else:
+        (q_o, s_o), z_o = oracle.quantize_sym(W[rows], g), None
+    c, s, z = q4.to_canonical(qw)
+    assert np.array_equal(to_np(c[torch.from_numpy(rows).cuda()]), oracle.pack_canonical(q_o))
+    assert np.array_equal(to_np(s[torch.from_numpy(rows).cuda()]).view(np.uint16), s_o.view(np.uint16))
+    for B in Bs:
+        x = synth.activation(B, K, seed=seed + B)
+        y = to_np(q4.gemm(to_gpu(x), qw))
+        ref = _ref_product(x, q_o, s_o, z_o, g)
+        rel, mx = assert_close(y[:, rows], ref, f"N={N} K={K} g={g} B={B}")
+        say(f"  N={N} K={K} g={g} B={B} asym={asym}: rel L2 {rel:.2e} max {mx:.2e}")
+
+
+def test_full_single_layer_b1(q4):
+    """4096x4096, B = 1: every output checked."""
+    W = synth.weight(4096, 4096, seed=0)
+    x = synth.activation(1, 4096, seed=0)
+    qw, q_o, s_o, _ = _check_quant_exact(q4, W, 128, False, device_layout=False)
+    y = to_np(q4.gemm(to_gpu(x), qw))
+    rel, mx = assert_close(y, _ref_product(x, q_o, s_o, None, 128), "4096x4096 B=1")
+    say(f"4096x4096 B=1 rel L2 {rel:.2e} max {mx:.2e}")
+
+
+@pytest.mark.parametrize("name", list(synth.LLAMA3_70B))
+def test_full_70b_shapes(q4, name):
+    N, K = synth.LLAMA3_70B[name]
+    say(f"70B {name} {N}x{K}")
+    _full_size_check(q4, N, K, 128, (1, 2, 4, 8), seed=3)
+
+
+@pytest.mark.parametrize("name", ["q_proj", "k_proj", "gate_proj", "down_proj"])
+def test_full_8b_shapes(q4, name):
+    N, K = synth.LLAMA3_8B[name]
+    say(f"8B {name} {N}x{K}")
+    _full_size_check(q4, N, K, 128, (1,), seed=2)
+
+
+def test_full_batch_sweep_28672x8192(q4):
+    say("28672x8192 batch sweep")
+    _full_size_check(q4, 28672, 8192, 128, (1, 4, 16, 32, 64, 128, 256), seed=4, nrows=64)
+
+
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_full_heavy_tailed_gemv(q4, g, asym):
+    say(f"heavy-tailed GEMV g={g} asym={asym}")
+    _full_size_check(q4, 14336, 4096, g, (1,), asym=asym, seed=5, heavy=True)

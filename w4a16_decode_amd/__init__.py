@@ -1,0 +1,28 @@
+"""w4a16_decode_amd: INT4 group-wise RTN weight quantization and the fused
+W4A16 GEMV / skinny GEMM for AMD MI355X (gfx950).
+
+Every computation runs in the HIP kernels of ``libq4.so`` behind the C ABI
+declared in ``include/q4.h``; this package only marshals torch tensors
+(device memory, the current HIP stream) into those calls. There is no CPU
+fallback: without the built library or a GPU the calls raise.
+"""
+
+from .ops import (  # noqa: F401
+    Q4Error,
+    QuantizedWeight,
+    from_canonical,
+    gemm,
+    gemm_config,
+    groups_count,
+    packed_bytes,
+    quantize_pack,
+    status_str,
+    to_canonical,
+    version,
+    workspace_bytes,
+)
+
+__all__ = [
+    "Q4Error", "QuantizedWeight", "quantize_pack", "gemm", "gemm_config", "to_canonical",
+    "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "status_str", "version",
+]

@@ -1,0 +1,55 @@
+// Host-side launch interfaces between the C ABI front end (q4_api.cpp) and the
+// kernel translation units. Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+struct QuantArgs {
+  const void* W;
+  int N, K, group;
+  int Np, Kp, Gp;
+  bool asym;
+  void* packed;
+  void* scales;
+  void* zeros;
+};
+
+struct LayoutArgs {
+  int N, K, group;
+  int Np, Kp, Gp;
+  bool asym;
+  // Device layout: read by to_canonical, written by from_canonical.
+  void* packed;
+  void* scales;
+  void* zeros;
+  // Canonical layout: written by to_canonical, read by from_canonical.
+  void* canon_codes;
+  void* canon_scales;
+  void* canon_zeros;
+};
+
+struct GemmArgs {
+  const void* x;
+  int B;
+  const void* packed;
+  const void* scales;
+  const void* zeros;
+  bool asym;
+  int N, K, group;
+  int Np, Kp, Gp;
+  void* y;
+  // launch shape
+  int rows_per_wave;    // row tiles of 16 per wavefront: 1, 2 or 4
+  int waves_per_group;  // wavefronts per workgroup splitting the channels: 1..16
+  int col_tiles;        // 16-column batch tiles per wavefront: 1, 2 or 4
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream);
+hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace q4

@@ -1,0 +1,354 @@
+// Quantize + pack kernels and the canonical <-> device layout converters.
+//
+// Method: group-wise round-to-nearest INT4 ("LLM 后训练量化深度实战…", www.ybb.press,
+// section 二: scale = group amax / 7, codes clamped to [-8, 7]); asymmetric uint4 with
+// integer zero point ("Post-training quantization: GPTQ, AWQ and rotation",
+// arganzheng.life, section 二.2; "压缩算法", cs-knowledge-wiki, section 7.4.1.1).
+//
+// One wavefront handles one 16-row x 128-channel tile (one 1 KiB output block):
+// lane l = r + 16*c reads, for m = 0..3, the 8 float16 weights of row r at
+// channels 32*m + 8*c .. +7 (16 bytes), which are exactly the 32 codes it will
+// store as its 16-byte slice of the block. A group of 128 channels of a row is
+// spread over the four lanes r, r+16, r+32, r+48; its amax is reduced across
+// them with two cross-lane exchanges. The quotient is an IEEE float32 division
+// rounded half-to-even (v_rndne_f32): dividing two float16 values this way makes
+// the same decision as the exact rational quotient.
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+struct Row8 {
+  float v[8];
+};
+
+__device__ __forceinline__ Row8 load_row8(const uint16_t* __restrict__ W, int n, int N, int k, int K) {
+  Row8 o;
+  if (n < N && k < K) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(W + (size_t)n * K + k);
+    const half8_t h = as_half8(raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = (float)h[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = 0.0f;
+  }
+  return o;
+}
+
+__device__ __forceinline__ float wave_max4(float a) {
+  // maximum over lanes l, l^16, l^32, l^48 (the four k-quarters of one row)
+  a = fmaxf(a, __shfl_xor(a, 16, 64));
+  a = fmaxf(a, __shfl_xor(a, 32, 64));
+  return a;
+}
+__device__ __forceinline__ float wave_min4(float a) {
+  a = fminf(a, __shfl_xor(a, 16, 64));
+  a = fminf(a, __shfl_xor(a, 32, 64));
+  return a;
+}
+
+__device__ __forceinline__ uint16_t half_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+// Symmetric scale of a group from its amax (float32 IEEE divide, RNE to float16).
+__device__ __forceinline__ _Float16 sym_scale(float amax) { return (_Float16)(fmaxf(amax, 1e-12f) / 7.0f); }
+
+__device__ __forceinline__ uint32_t sym_code(float w, float s) {
+  // offset-binary nibble q + 8, q = clamp(rint(w / s), -8, 7); 0 code for s == 0
+  if (s == 0.0f) return 8u;
+  float q = rintf(w / s);
+  q = fminf(fmaxf(q, -8.0f), 7.0f);
+  return (uint32_t)((int)q + 8);
+}
+
+__device__ __forceinline__ uint32_t asym_code(float w, float s, float z) {
+  if (s == 0.0f) return 0u;
+  float q = rintf(w / s) + z;
+  q = fminf(fmaxf(q, 0.0f), 15.0f);
+  return (uint32_t)q;
+}
+
+__device__ __forceinline__ uint32_t pack_dword(const uint32_t nib[8]) {
+  uint32_t d = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) d |= nib[e] << (4 * nibble_of(e));
+  return d;
+}
+
+// GSUB = groups per 128-channel block (4: g = 32, 2: g = 64, 1: g = 128).
+template <int GSUB, bool ASYM>
+__global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ W, int N, int K, int S,
+                                                          int Gp, int64_t units, uint4* __restrict__ packed,
+                                                          uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  constexpr int MPG = 4 / GSUB;  // 32-channel steps per group
+
+  for (int64_t u = wave; u < units; u += nwaves) {
+    const int t = (int)(u / S), s = (int)(u % S);
+    const int n = t * kTileRows + r;
+    Row8 w[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+
+    uint32_t dw[4];
+#pragma unroll
+    for (int gs = 0; gs < GSUB; ++gs) {
+      float scale_f;
+      float zero_f = 0.0f;
+      _Float16 s16;
+      if (!ASYM) {
+        float a = 0.0f;
+#pragma unroll
+        for (int m = gs * MPG; m < (gs + 1) * MPG; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(w[m].v[e]));
+        a = wave_max4(a);
+        s16 = sym_scale(a);
+        scale_f = (float)s16;
+      } else {
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int m = gs * MPG; m < (gs + 1) * MPG; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lo = fminf(lo, w[m].v[e]);
+            hi = fmaxf(hi, w[m].v[e]);
+          }
+        lo = wave_min4(lo);
+        hi = wave_max4(hi);
+        s16 = (_Float16)((hi - lo) / 15.0f);
+        scale_f = (float)s16;
+        if (scale_f != 0.0f) zero_f = fminf(fmaxf(rintf(-lo / scale_f), 0.0f), 15.0f);
+      }
+#pragma unroll
+      for (int m = gs * MPG; m < (gs + 1) * MPG; ++m) {
+        uint32_t nib[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          nib[e] = ASYM ? asym_code(w[m].v[e], scale_f, zero_f) : sym_code(w[m].v[e], scale_f);
+        dw[m] = pack_dword(nib);
+      }
+      if (c == 0) {
+        const size_t gi = ((size_t)t * Gp + (size_t)s * GSUB + gs) * kTileRows + r;
+        scales[gi] = half_bits(s16);
+        if (ASYM) zeros[gi] = (uint8_t)zero_f;
+      }
+    }
+    packed[((size_t)t * S + s) * kWave + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+}
+
+// Groups of g = 128*J channels, J >= 2: one wavefront per (tile, group); the
+// group's blocks are read twice (reduction pass, then coding pass).
+template <bool ASYM>
+__global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restrict__ W, int N, int K, int S, int J,
+                                                         int Gp, int64_t units, uint4* __restrict__ packed,
+                                                         uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+
+  for (int64_t u = wave; u < units; u += nwaves) {
+    const int t = (int)(u / Gp), j = (int)(u % Gp);
+    const int n = t * kTileRows + r;
+    float a = 0.0f, lo = INFINITY, hi = -INFINITY;
+    for (int sb = 0; sb < J; ++sb) {
+      const int s = j * J + sb;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a = fmaxf(a, fabsf(w.v[e]));
+          lo = fminf(lo, w.v[e]);
+          hi = fmaxf(hi, w.v[e]);
+        }
+      }
+    }
+    _Float16 s16;
+    float scale_f, zero_f = 0.0f;
+    if (!ASYM) {
+      s16 = sym_scale(wave_max4(a));
+      scale_f = (float)s16;
+    } else {
+      lo = wave_min4(lo);
+      hi = wave_max4(hi);
+      s16 = (_Float16)((hi - lo) / 15.0f);
+      scale_f = (float)s16;
+      if (scale_f != 0.0f) zero_f = fminf(fmaxf(rintf(-lo / scale_f), 0.0f), 15.0f);
+    }
+    for (int sb = 0; sb < J; ++sb) {
+      const int s = j * J + sb;
+      uint32_t dw[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+        uint32_t nib[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nib[e] = ASYM ? asym_code(w.v[e], scale_f, zero_f) : sym_code(w.v[e], scale_f);
+        dw[m] = pack_dword(nib);
+      }
+      packed[((size_t)t * S + s) * kWave + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    }
+    if (c == 0) {
+      const size_t gi = ((size_t)t * Gp + j) * kTileRows + r;
+      scales[gi] = half_bits(s16);
+      if (ASYM) zeros[gi] = (uint8_t)zero_f;
+    }
+  }
+}
+
+// ---- layout converters -------------------------------------------------------
+
+__device__ __forceinline__ size_t dev_dword_index(int n, int k, int S) {
+  const int t = n >> 4, r = n & 15, s = k >> 7, m = (k & 127) >> 5, c = (k & 31) >> 3;
+  return (((size_t)t * S + s) * kWave + r + 16 * c) * 4 + m;
+}
+
+__global__ void to_canonical_codes_kernel(const uint32_t* __restrict__ packed, int N, int K, int S, bool asym,
+                                          uint8_t* __restrict__ canon) {
+  const int64_t total = (int64_t)N * (K / 2);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / (K / 2));
+    const int k = (int)(i % (K / 2)) * 2;
+    const uint32_t d = packed[dev_dword_index(n, k, S)];
+    uint32_t lo = (d >> (4 * nibble_of(k & 7))) & 0xF;
+    uint32_t hi = (d >> (4 * nibble_of((k + 1) & 7))) & 0xF;
+    if (!asym) {  // offset binary -> 4-bit two's complement: (v - 8) mod 16 == v ^ 8
+      lo ^= 8u;
+      hi ^= 8u;
+    }
+    canon[i] = (uint8_t)(lo | (hi << 4));
+  }
+}
+
+__global__ void from_canonical_codes_kernel(const uint8_t* __restrict__ canon, int N, int K, int S, bool asym,
+                                            int64_t dwords, uint32_t* __restrict__ packed) {
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < dwords; d += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(d & 3);
+    const int64_t chunk = d >> 2;
+    const int lane = (int)(chunk & 63);
+    const int64_t ts = chunk >> 6;
+    const int t = (int)(ts / S), s = (int)(ts % S);
+    const int n = t * 16 + (lane & 15);
+    const int k0 = s * kSuperK + m * kBlockK + 8 * (lane >> 4);
+    uint32_t out = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      uint32_t v;
+      if (n < N && k < K) {
+        v = (canon[(size_t)n * (K / 2) + (k >> 1)] >> (4 * (k & 1))) & 0xF;
+        if (!asym) v ^= 8u;
+      } else {
+        v = asym ? 0u : 8u;
+      }
+      out |= v << (4 * nibble_of(e));
+    }
+    packed[d] = out;
+  }
+}
+
+template <typename T>
+__global__ void groups_to_canonical_kernel(const T* __restrict__ dev, int N, int G, int Gp, T* __restrict__ canon) {
+  const int64_t total = (int64_t)N * G;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / G), j = (int)(i % G);
+    canon[i] = dev[((size_t)(n >> 4) * Gp + j) * 16 + (n & 15)];
+  }
+}
+
+template <typename T>
+__global__ void groups_from_canonical_kernel(const T* __restrict__ canon, int N, int G, int Gp, int64_t total,
+                                             T* __restrict__ dev) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i & 15);
+    const int64_t tj = i >> 4;
+    const int t = (int)(tj / Gp), j = (int)(tj % Gp);
+    const int n = t * 16 + r;
+    dev[i] = (n < N && j < G) ? canon[(size_t)n * G + j] : (T)0;
+  }
+}
+
+inline int grid_for(int64_t work, int block) {
+  int64_t g = (work + block - 1) / block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+  const int S = a.Kp / kSuperK;
+  const int T = a.Np / kTileRows;
+  const int block = 256;
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  uint4* P = static_cast<uint4*>(a.packed);
+  uint16_t* Sc = static_cast<uint16_t*>(a.scales);
+  uint8_t* Z = static_cast<uint8_t*>(a.zeros);
+  if (a.group <= kSuperK) {
+    const int64_t units = (int64_t)T * S;
+    const int grid = grid_for(units * kWave, block);
+    if (a.group == 32) {
+      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<4, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+      else hipLaunchKernelGGL((quant_block_kernel<4, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+    } else if (a.group == 64) {
+      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<2, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+      else hipLaunchKernelGGL((quant_block_kernel<2, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+    } else {
+      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<1, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+      else hipLaunchKernelGGL((quant_block_kernel<1, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+    }
+  } else {
+    const int J = a.group / kSuperK;
+    const int64_t units = (int64_t)T * a.Gp;
+    const int grid = grid_for(units * kWave, block);
+    if (a.asym) hipLaunchKernelGGL((quant_wide_kernel<true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z);
+    else hipLaunchKernelGGL((quant_wide_kernel<false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream) {
+  const int S = a.Kp / kSuperK;
+  const int G = a.K / a.group;
+  const int block = 256;
+  hipLaunchKernelGGL(to_canonical_codes_kernel, dim3(grid_for((int64_t)a.N * (a.K / 2), block)), dim3(block), 0,
+                     stream, static_cast<const uint32_t*>(a.packed), a.N, a.K, S, a.asym,
+                     static_cast<uint8_t*>(a.canon_codes));
+  hipLaunchKernelGGL((groups_to_canonical_kernel<uint16_t>), dim3(grid_for((int64_t)a.N * G, block)), dim3(block), 0,
+                     stream, static_cast<const uint16_t*>(a.scales), a.N, G, a.Gp,
+                     static_cast<uint16_t*>(a.canon_scales));
+  if (a.asym)
+    hipLaunchKernelGGL((groups_to_canonical_kernel<uint8_t>), dim3(grid_for((int64_t)a.N * G, block)), dim3(block), 0,
+                       stream, static_cast<const uint8_t*>(a.zeros), a.N, G, a.Gp,
+                       static_cast<uint8_t*>(a.canon_zeros));
+  return hipGetLastError();
+}
+
+hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream) {
+  const int S = a.Kp / kSuperK;
+  const int G = a.K / a.group;
+  const int block = 256;
+  const int64_t dwords = (int64_t)a.Np * a.Kp / 8;
+  const int64_t gtotal = (int64_t)a.Np * a.Gp;
+  hipLaunchKernelGGL(from_canonical_codes_kernel, dim3(grid_for(dwords, block)), dim3(block), 0, stream,
+                     static_cast<const uint8_t*>(a.canon_codes), a.N, a.K, S, a.asym, dwords,
+                     static_cast<uint32_t*>(a.packed));
+  hipLaunchKernelGGL((groups_from_canonical_kernel<uint16_t>), dim3(grid_for(gtotal, block)), dim3(block), 0, stream,
+                     static_cast<const uint16_t*>(a.canon_scales), a.N, G, a.Gp, gtotal,
+                     static_cast<uint16_t*>(a.scales));
+  if (a.asym)
+    hipLaunchKernelGGL((groups_from_canonical_kernel<uint8_t>), dim3(grid_for(gtotal, block)), dim3(block), 0, stream,
+                       static_cast<const uint8_t*>(a.canon_zeros), a.N, G, a.Gp, gtotal,
+                       static_cast<uint8_t*>(a.zeros));
+  return hipGetLastError();
+}
+
+}  // namespace q4

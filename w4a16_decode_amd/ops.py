@@ -1,0 +1,207 @@
+"""torch-facing wrappers over the libq4 C ABI (same names as the C calls).
+
+These functions check tensor dtypes, devices and shapes, allocate outputs with
+torch on the tensors' device, and pass raw pointers plus torch's current HIP
+stream to libq4. They do no arithmetic of their own.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import _lib
+
+SUPPORTED_GROUPS_NOTE = "32, 64 or a multiple of 128"
+
+
+class Q4Error(RuntimeError):
+    """A libq4 call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_str(status)} ({status}): {message}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Q4Error(status, _lib.load().q4_last_error().decode())
+
+
+def status_str(status: int) -> str:
+    return _lib.load().q4_status_str(int(status)).decode()
+
+
+def version() -> str:
+    return _lib.load().q4_version().decode()
+
+
+def packed_bytes(out_features: int, in_features: int) -> int:
+    return int(_lib.load().q4_packed_bytes(out_features, in_features))
+
+
+def groups_count(out_features: int, in_features: int, group: int) -> int:
+    return int(_lib.load().q4_groups_count(out_features, in_features, group))
+
+
+def workspace_bytes(batch: int, out_features: int, in_features: int, group: int) -> int:
+    return int(_lib.load().q4_workspace_bytes(batch, out_features, in_features, group))
+
+
+def _stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require_gpu(t, name: str, dtype) -> None:
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU (got {t.device}); libq4 has no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class QuantizedWeight:
+    """Device-layout INT4 weights of an [out_features, in_features] matrix."""
+
+    packed: object          # uint8 [packed_bytes(out, in)]
+    scales: object          # float16 [groups_count(out, in, group)]
+    zeros: object | None    # uint8 [groups_count(...)] for asymmetric weights
+    out_features: int
+    in_features: int
+    group: int
+    asym: bool = False
+
+    @property
+    def device(self):
+        return self.packed.device
+
+    def nbytes(self) -> int:
+        n = self.packed.numel() + 2 * self.scales.numel()
+        if self.zeros is not None:
+            n += self.zeros.numel()
+        return n
+
+
+def _alloc_qw(out_features: int, in_features: int, group: int, asym: bool, device) -> QuantizedWeight:
+    import torch
+
+    nb = packed_bytes(out_features, in_features)
+    ng = groups_count(out_features, in_features, group)
+    if nb == 0 or ng == 0:
+        lib = _lib.load()
+        raise Q4Error(3 if nb else 2, lib.q4_last_error().decode() or
+                      f"invalid shape [{out_features}, {in_features}] / group {group} ({SUPPORTED_GROUPS_NOTE})")
+    packed = torch.empty(nb, dtype=torch.uint8, device=device)
+    scales = torch.empty(ng, dtype=torch.float16, device=device)
+    zeros = torch.empty(ng, dtype=torch.uint8, device=device) if asym else None
+    return QuantizedWeight(packed, scales, zeros, out_features, in_features, group, asym)
+
+
+def quantize_pack(W, group: int = 128, asym: bool = False) -> QuantizedWeight:
+    """q4_quantize_pack / q4_quantize_pack_asym on a float16 [out, in] GPU tensor."""
+    import torch
+
+    _require_gpu(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [out_features, in_features]")
+    out_features, in_features = W.shape
+    qw = _alloc_qw(out_features, in_features, group, asym, W.device)
+    lib = _lib.load()
+    if asym:
+        st = lib.q4_quantize_pack_asym(W.data_ptr(), out_features, in_features, group, qw.packed.data_ptr(),
+                                       qw.scales.data_ptr(), qw.zeros.data_ptr(), _stream(W))
+    else:
+        st = lib.q4_quantize_pack(W.data_ptr(), out_features, in_features, group, qw.packed.data_ptr(),
+                                  qw.scales.data_ptr(), _stream(W))
+    _check(st)
+    return qw
+
+
+def _prep_gemm(x, qw: QuantizedWeight, out):
+    import torch
+
+    _require_gpu(x, "x", torch.float16)
+    if x.dim() != 2 or x.shape[1] != qw.in_features:
+        raise ValueError(f"x must be [B, {qw.in_features}]")
+    B = x.shape[0]
+    if out is None:
+        out = torch.empty((B, qw.out_features), dtype=torch.float16, device=x.device)
+    else:
+        _require_gpu(out, "out", torch.float16)
+        if tuple(out.shape) != (B, qw.out_features):
+            raise ValueError(f"out must be [{B}, {qw.out_features}]")
+    return B, out
+
+
+def gemm(x, qw: QuantizedWeight, out=None, workspace=None):
+    """q4_gemm / q4_gemm_asym: y = x . W_hat^T, float16 [B, out_features]."""
+    B, out = _prep_gemm(x, qw, out)
+    lib = _lib.load()
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if qw.asym:
+        st = lib.q4_gemm_asym(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.zeros.data_ptr(),
+                              qw.out_features, qw.in_features, qw.group, out.data_ptr(), ws_ptr, ws_bytes,
+                              _stream(x))
+    else:
+        st = lib.q4_gemm(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.out_features,
+                         qw.in_features, qw.group, out.data_ptr(), ws_ptr, ws_bytes, _stream(x))
+    _check(st)
+    return out
+
+
+def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int, out=None):
+    """q4_gemm_config: q4_gemm with an explicit launch shape (tuning)."""
+    B, out = _prep_gemm(x, qw, out)
+    lib = _lib.load()
+    st = lib.q4_gemm_config(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(),
+                            qw.zeros.data_ptr() if qw.zeros is not None else None, int(qw.asym),
+                            qw.out_features, qw.in_features, qw.group, out.data_ptr(), rows_per_wave,
+                            waves_per_group, _stream(x))
+    _check(st)
+    return out
+
+
+def to_canonical(qw: QuantizedWeight):
+    """q4_to_canonical: (codes uint8 [out, in/2], scales float16 [out, in/g], zeros uint8 or None)."""
+    import torch
+
+    N, K, g = qw.out_features, qw.in_features, qw.group
+    dev = qw.packed.device
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // g), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, K // g), dtype=torch.uint8, device=dev) if qw.asym else None
+    lib = _lib.load()
+    st = lib.q4_to_canonical(qw.packed.data_ptr(), qw.scales.data_ptr(),
+                             qw.zeros.data_ptr() if qw.asym else None, int(qw.asym), N, K, g, codes.data_ptr(),
+                             scales.data_ptr(), zeros.data_ptr() if qw.asym else None, _stream(qw.packed))
+    _check(st)
+    return codes, scales, zeros
+
+
+def from_canonical(codes, scales, group: int, zeros=None) -> QuantizedWeight:
+    """q4_from_canonical: canonical codes/scales(/zeros) on the GPU -> device layout."""
+    import torch
+
+    _require_gpu(codes, "codes", torch.uint8)
+    _require_gpu(scales, "scales", torch.float16)
+    asym = zeros is not None
+    if asym:
+        _require_gpu(zeros, "zeros", torch.uint8)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    if tuple(scales.shape) != (N, K // group) or (asym and tuple(zeros.shape) != (N, K // group)):
+        raise ValueError("scales/zeros must be [out, in/group]")
+    qw = _alloc_qw(N, K, group, asym, codes.device)
+    lib = _lib.load()
+    st = lib.q4_from_canonical(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr() if asym else None, int(asym),
+                               N, K, group, qw.packed.data_ptr(), qw.scales.data_ptr(),
+                               qw.zeros.data_ptr() if asym else None, _stream(codes))
+    _check(st)
+    return qw
