@@ -69,13 +69,19 @@ class Sweep:
 
         import synth
 
+        import w4a16_decode_amd as q4
+
         self.model = model
         self.B = B
         self.xs, self.ys = [], []
+        ws = 0
         for layer, mats in enumerate(model):
-            for i, (_, N, K, _) in enumerate(mats):
+            for i, (_, N, K, qw) in enumerate(mats):
                 self.xs.append(synth.device_activation(B, K, seed=seed, layer=layer, matrix=100 + i, device=device))
                 self.ys.append(torch.empty((B, N), dtype=torch.float16, device=device))
+                ws = max(ws, q4.workspace_bytes(B, N, K, qw.group))
+        # one scratch buffer shared by the launches (they run in stream order)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
         self.graph = None
 
     def launches(self):
@@ -89,7 +95,7 @@ class Sweep:
         import w4a16_decode_amd as q4
 
         for _, x, qw, y in self.launches():
-            q4.gemm(x, qw, out=y)
+            q4.gemm(x, qw, out=y, workspace=self.ws)
 
     def capture(self):
         import torch
@@ -139,11 +145,11 @@ class Sweep:
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
-                    q4.gemm(x, qw, out=y)
+                    q4.gemm(x, qw, out=y, workspace=self.ws)
                     b.record(stream)
                     evs.append((a, b, qw))
                 else:
-                    q4.gemm(x, qw, out=y)
+                    q4.gemm(x, qw, out=y, workspace=self.ws)
             torch.cuda.synchronize()
             durs += [(a.elapsed_time(b) / 1e3, qw) for a, b, qw in evs]
         return durs

@@ -114,8 +114,10 @@ q4_status q4_quantize_pack(const void* W, int64_t out, int64_t in, int32_t group
 q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t group,
                                 void* packed, void* scales, void* zeros, void* stream);
 
-/* Bytes of workspace q4_gemm needs for this shape (0 in this version: the
- * k-split is reduced inside each workgroup, no scratch memory is used). */
+/* Bytes of device workspace q4_gemm / q4_gemm_asym need for this shape: float32
+ * partial sums when the channel range is split over several workgroups (B <= 16
+ * with a long `in`, or too few rows to fill the GPU); 0 when none is needed. The
+ * workspace is scratch: its contents on entry are ignored and undefined on return. */
 size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group);
 
 /* Fused W4A16 product ([ARG] sections 二.2 and 二.3; [YBB] section 一):
@@ -125,7 +127,9 @@ size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group);
  * GEMV kernel (one 16-column MFMA tile, padded), larger B the skinny-GEMM
  * tiling. x: [B][in] float16, 16-byte aligned; packed/scales as written by
  * q4_quantize_pack; y: [B][out] float16, 2-byte aligned.
- * `workspace` may be NULL when q4_workspace_bytes() returns 0. */
+ * `workspace` (16-byte aligned) must hold q4_workspace_bytes(B, out, in, group)
+ * bytes; it may be NULL when that is 0, else Q4_ERR_WORKSPACE is returned.
+ * Results are deterministic: partial sums are added in a fixed order. */
 q4_status q4_gemm(const void* x, int64_t B, const void* packed, const void* scales,
                   int64_t out, int64_t in, int32_t group, void* y,
                   void* workspace, size_t workspace_bytes, void* stream);
@@ -137,11 +141,15 @@ q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void*
 
 /* q4_gemm with an explicit launch shape, for tuning: `rows_per_wave` row tiles
  * of 16 per wavefront (1, 2 or 4), `waves_per_group` wavefronts per workgroup
- * (1..16) splitting the in dimension. Returns Q4_ERR_UNSUPPORTED for shapes
- * outside those ranges. `asym` selects q4_gemm_asym semantics (zeros used). */
+ * (1..8) splitting the channel range, `k_splits` workgroups splitting it further
+ * (B <= 16 only; 1 otherwise). Needs k_splits * B * out * 4 bytes of workspace
+ * when k_splits > 1. Returns Q4_ERR_UNSUPPORTED for shapes the kernels cannot
+ * run (e.g. an activation slice larger than the 64 KiB LDS budget). `asym`
+ * selects q4_gemm_asym semantics (zeros used). */
 q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales,
                          const void* zeros, int32_t asym, int64_t out, int64_t in, int32_t group,
-                         void* y, int32_t rows_per_wave, int32_t waves_per_group, void* stream);
+                         void* y, int32_t rows_per_wave, int32_t waves_per_group, int32_t k_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device layout -> canonical layout (see above). `zeros`/`canon_zeros` are used
  * only when asym != 0. canon_codes: out*in/2 bytes; canon_scales: out*(in/group)

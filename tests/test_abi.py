@@ -60,7 +60,6 @@ def test_sizes(lib):
     assert lib.q4_groups_count(4096, 4096, 128) == 4096 * 32
     assert lib.q4_groups_count(20, 96, 32) == 32 * 4            # Gp = ceil(96/128)*128/32
     assert lib.q4_groups_count(20, 96, 64) == 0                  # 96 % 64 != 0
-    assert lib.q4_workspace_bytes(1, 4096, 4096, 128) == 0
     for g, ok in ((32, 1), (64, 1), (128, 1), (256, 1), (4096, 1), (96, 0), (16, 0), (0, 0), (-128, 0), (192, 0)):
         assert lib.q4_group_supported(g) == ok, g
 
@@ -94,10 +93,28 @@ def test_gemm_validation(lib):
     assert g(FAKE, 1, FAKE, FAKE, 16, 128, 128, FAKE + 1, None, 0, None) == 4
     assert lib.q4_gemm_asym(FAKE, 1, FAKE, FAKE, None, 16, 128, 128, FAKE, None, 0, None) == 1
     c = lib.q4_gemm_config
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 3, 1, None) == 5
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 9, None) == 5
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 0, 0, None) == 5
-    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 8, None) == 5  # reduction buffer too big
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 3, 1, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 9, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 0, 0, 0, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 8, 3, None, 0, None) == 5   # k_splits > blocks
+    assert c(FAKE, 16, FAKE, FAKE, None, 0, 16, 8192, 128, FAKE, 1, 8, 1, None, 0, None) == 5  # x slice > LDS
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 8, 1, None, 0, None) == 5   # B > 16, R*NT > 4
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 8, 2, None, 0, None) == 5   # k_splits, B > 16
+    # split k needs workspace: 2 * 1 * 16 * 4 bytes here
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, None, 0, None) == 6
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, FAKE, 64, None) == 6
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, FAKE + 4, 128, None) == 4
+
+
+def test_workspace_sizes(lib):
+    # B = 1 on a long row: the 56 KiB activation slice fits one workgroup's LDS
+    assert lib.q4_workspace_bytes(1, 4096, 4096, 128) == 0
+    # B = 8 over 28672 channels cannot stage the whole row: split over workgroups
+    ws = lib.q4_workspace_bytes(8, 8192, 28672, 128)
+    assert ws > 0 and ws % (8 * 8192 * 4) == 0
+    assert lib.q4_workspace_bytes(0, 8192, 28672, 128) == 0
+    assert lib.q4_workspace_bytes(64, 8192, 8192, 128) == 0
+    assert lib.q4_gemm(FAKE, 8, FAKE, FAKE, 8192, 28672, 128, FAKE, None, 0, None) == 6
 
 
 def test_layout_validation(lib):

@@ -5,6 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/q4.h"
@@ -61,23 +65,85 @@ q4_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// Launch shape for y = x W^T with B rows (the kernel is described at the top of
-// q4_gemm.hip). Aim for several thousand wavefronts so every CU keeps enough
-// 16-byte loads in flight, with at least two 1 KiB blocks per wavefront.
+// Launch shape for y = x W^T with B rows (the kernels are described at the top of
+// q4_gemm.hip). B <= 16 runs the persistent GEMV kernel: every workgroup keeps its
+// slice of x (B rows x its channel range) in LDS next to two reduction buffers, so
+// the channel range is split over KS workgroups until that fits the device's LDS.
+constexpr int kGemvXChunks = 8;          // x chunks of 16 B per thread (kXChunksPerThread)
+constexpr size_t kLdsFallback = 64 * 1024;
+
+// LDS a workgroup may allocate on the current device (64 KiB if it cannot be queried).
+size_t lds_per_block() {
+  static std::mutex mu;
+  static std::map<int, size_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kLdsFallback;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int v = 0;
+  size_t lim = kLdsFallback;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+    lim = (size_t)v;
+  cache[dev] = lim;
+  return lim;
+}
+
+// LDS of one GEMV workgroup holding one row block (q4_gemm.hip, GemvLds): x slice
+// + zero row, the per-unit biases of symmetric codes (sized for g = 32, the most
+// units), two reduction buffers and the result buffer of one row block. The launch
+// adds result space for further row blocks only within a fixed 16 KiB.
+size_t gemv_lds(int B, int S, int KS, int W, int R) {
+  const size_t nsb = (size_t)((S + KS - 1) / KS);
+  const size_t x = (((size_t)B * (nsb * 128 + 8) + 128) * 2 + 15) & ~(size_t)15;
+  const size_t beta = ((size_t)B * nsb * 4 + 1 + 3) / 4 * 4 * sizeof(float);
+  return x + beta + 2 * (size_t)W * R * 1024 + 16 * 1024;
+}
+
+bool gemv_shape_ok(int B, int S, int KS, int W, int R, size_t lds_limit) {
+  if (KS < 1 || KS > S || W < 1 || W > 8 || W > S / KS) return false;
+  const int nsb = (S + KS - 1) / KS;
+  if (gemv_lds(B, S, KS, W, R) > lds_limit) return false;
+  return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
+}
+
 void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
   const int T = d.Np / 16;
   const int S = d.Kp / 128;
   const int col_tiles_total = (B + 15) / 16;
-  a->col_tiles = col_tiles_total <= 1 ? 1 : col_tiles_total == 2 ? 2 : 4;
+  if (B <= 16) {
+    // at most half of a 160 KiB CU, so two 8-wavefront workgroups stay resident
+    const size_t lim = std::min<size_t>(lds_per_block(), 80 * 1024);
+    a->col_tiles = 1;
+    int R = T >= 2048 ? 2 : 1;
+    int W = std::min(8, S);
+    int KS = 1;
+    while (!gemv_shape_ok(B, S, KS, W, R, lim)) {
+      if (R > 1) { R = 1; continue; }
+      if (KS < S && W <= S / (KS + 1)) { ++KS; continue; }
+      if (W > 1) { W /= 2; KS = 1; continue; }
+      break;  // unreachable for B <= 16: KS = S, W = 1 always fits
+    }
+    a->rows_per_wave = R;
+    a->waves_per_group = W;
+    a->k_splits = KS;
+    return;
+  }
+  a->col_tiles = col_tiles_total == 2 ? 2 : 4;
   const int col_groups = (col_tiles_total + a->col_tiles - 1) / a->col_tiles;
-  int R = (T >= 2048) ? 4 : (T >= 512 ? 2 : 1);
-  if (a->col_tiles == 4 && R > 2) R = 2;
+  int R = (T >= 512) ? 2 : 1;
+  if (a->col_tiles == 4) R = 1;
   const int64_t wgs = (int64_t)((T + R - 1) / R) * col_groups;
   int W = 1;
   while (W < 8 && wgs * W < 4096 && S / (2 * W) >= 1) W *= 2;
-  while (W > 1 && (int64_t)W * R * a->col_tiles * 1024 > 64 * 1024) W /= 2;
+  while (W > 1 && (int64_t)W * R * a->col_tiles * 1024 > (int64_t)kLdsFallback) W /= 2;
   a->rows_per_wave = R;
   a->waves_per_group = W;
+  a->k_splits = 1;
+}
+
+size_t splits_workspace(const q4::GemmArgs& a) {
+  return a.k_splits > 1 ? (size_t)a.k_splits * a.B * a.N * sizeof(float) : 0;
 }
 
 }  // namespace
@@ -115,7 +181,15 @@ size_t q4_groups_count(int64_t out, int64_t in, int32_t group) {
   return (size_t)d.Np * (size_t)d.Gp;
 }
 
-size_t q4_workspace_bytes(int64_t, int64_t, int64_t, int32_t) { return 0; }
+size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group) {
+  Dims d;
+  if (B <= 0 || B >= kMaxDim || check_dims(out, in, group, &d) != Q4_OK) return 0;
+  q4::GemmArgs a{};
+  a.B = (int)B;
+  a.N = d.N;
+  pick_shape((int)B, d, &a);
+  return splits_workspace(a);
+}
 
 static q4_status quantize_common(const void* W, int64_t out, int64_t in, int32_t group, void* packed, void* scales,
                                  void* zeros, bool asym, void* stream) {
@@ -141,7 +215,8 @@ q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t 
 
 static q4_status gemm_common(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                              bool asym, int64_t out, int64_t in, int32_t group, void* y, int rows_per_wave,
-                             int waves_per_group, void* stream) {
+                             int waves_per_group, int k_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   if (B < 0 || B >= kMaxDim) return fail(Q4_ERR_SHAPE, "B=%lld out of range", (long long)B);
   Dims d;
   q4_status st = check_dims(out, in, group, &d);
@@ -168,41 +243,59 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
   a.Gp = d.Gp;
   a.y = y;
   pick_shape((int)B, d, &a);
-  if (rows_per_wave > 0 || waves_per_group > 0) {
+  if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0) {
     if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
       return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave must be 1, 2 or 4");
     if (waves_per_group < 1 || waves_per_group > 8)
       return fail(Q4_ERR_UNSUPPORTED, "waves_per_group must be in [1, 8]");
-    if ((int64_t)waves_per_group * rows_per_wave * a.col_tiles * 1024 > 64 * 1024)
-      return fail(Q4_ERR_UNSUPPORTED, "waves_per_group * rows_per_wave * column tiles exceeds the 64 KiB reduction buffer");
+    if (B <= 16) {
+      if (!gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, lds_per_block()))
+        return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: the activation slice of B=%lld and "
+                    "the reduction buffers exceed LDS, or fewer than one 128-channel block per wavefront",
+                    (int)k_splits, (int)waves_per_group, (long long)B);
+    } else {
+      if (k_splits != 1) return fail(Q4_ERR_UNSUPPORTED, "k_splits must be 1 for B > 16");
+      if (rows_per_wave * a.col_tiles > 4)
+        return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave * column tiles must be <= 4 for B > 16");
+      if ((int64_t)waves_per_group * rows_per_wave * a.col_tiles * 1024 > (int64_t)kLdsFallback)
+        return fail(Q4_ERR_UNSUPPORTED, "waves_per_group * rows_per_wave * column tiles exceeds the reduction buffer");
+    }
     a.rows_per_wave = rows_per_wave;
     a.waves_per_group = waves_per_group;
+    a.k_splits = k_splits;
   }
+  const size_t need = splits_workspace(a);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(Q4_ERR_WORKSPACE, "this shape needs %zu bytes of workspace (q4_workspace_bytes), got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(Q4_ERR_ALIGN, "workspace needs 16-byte alignment");
+  }
+  a.workspace = workspace;
   return hip_status(q4::launch_gemm(a, static_cast<hipStream_t>(stream)), "gemm launch");
 }
 
 q4_status q4_gemm(const void* x, int64_t B, const void* packed, const void* scales, int64_t out, int64_t in,
                   int32_t group, void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, stream);
+  return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, 0, workspace, workspace_bytes,
+                     stream);
 }
 
 q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                        int64_t out, int64_t in, int32_t group, void* y, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return gemm_common(x, B, packed, scales, zeros, true, out, in, group, y, 0, 0, stream);
+  return gemm_common(x, B, packed, scales, zeros, true, out, in, group, y, 0, 0, 0, workspace, workspace_bytes,
+                     stream);
 }
 
 q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                          int32_t asym, int64_t out, int64_t in, int32_t group, void* y, int32_t rows_per_wave,
-                         int32_t waves_per_group, void* stream) {
-  if (rows_per_wave <= 0 || waves_per_group <= 0)
-    return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave and waves_per_group must be positive");
+                         int32_t waves_per_group, int32_t k_splits, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (rows_per_wave <= 0 || waves_per_group <= 0 || k_splits <= 0)
+    return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave, waves_per_group and k_splits must be positive");
   return gemm_common(x, B, packed, scales, zeros, asym != 0, out, in, group, y, rows_per_wave, waves_per_group,
-                     stream);
+                     k_splits, workspace, workspace_bytes, stream);
 }
 
 q4_status q4_to_canonical(const void* packed, const void* scales, const void* zeros, int32_t asym, int64_t out,

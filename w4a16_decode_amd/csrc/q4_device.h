@@ -18,6 +18,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 16;      // rows per tile (MFMA M)
 constexpr int kSuperK = 128;       // input channels per 1 KiB block
@@ -50,5 +51,58 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t bias_lo, half2_t
 }
 
 __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+
+// A 32-bit constant held in a VGPR. gfx9 VOP3 encodings take no literal operand,
+// so (w & mask) | magic only becomes one v_and_or_b32 when mask and magic are
+// registers; the asm is a plain register move the compiler cannot fold back.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// Workgroup barrier for LDS-only communication: waits for this wavefront's LDS
+// operations, not for its outstanding global loads. __syncthreads() also waits for
+// every vector-memory load in flight (vmcnt(0)), which would drain the prefetched
+// weight pipeline at each barrier. The "memory" clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The magic-number masks of dequant8 as VGPR operands.
+struct DequantRegs {
+  uint32_t lo, hi, magic;
+  __device__ __forceinline__ static DequantRegs make() {
+    return DequantRegs{vreg_const(0x000F000Fu), vreg_const(0x00F000F0u), vreg_const(0x64006400u)};
+  }
+};
+
+// dequant8 with register masks: 1 shift + 4 v_and_or_b32 + 4 packed f16 ops per 8 codes.
+__device__ __forceinline__ half8_t dequant8r(uint32_t w, const DequantRegs& k, half2_t bias_lo, half2_t bias_hi) {
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t t = w >> 8;
+  half2_t p0 = as_half2((w & k.lo) | k.magic) + bias_lo;
+  half2_t p1 = __builtin_elementwise_fma(as_half2((w & k.hi) | k.magic), sixteenth, bias_hi);
+  half2_t p2 = as_half2((t & k.lo) | k.magic) + bias_lo;
+  half2_t p3 = __builtin_elementwise_fma(as_half2((t & k.hi) | k.magic), sixteenth, bias_hi);
+  half4_t lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  half4_t hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Raw magic-number halves of 8 codes for the symmetric GEMV: the MFMA operand
+// holds 1024 + n (elements 0, 1, 4, 5) and 1024 + 16 n (elements 2, 3, 6, 7), with
+// n = q + 8. The kernel pairs them with x (resp. x/16) and subtracts the bias
+// 1032 * sum(x at plain elements) + 1152 * sum(x/16 at scaled elements) from the
+// float32 partial sum, which leaves exactly sum(q * x): 1 shift + 4 v_and_or_b32.
+__device__ __forceinline__ half8_t magic8r(uint32_t w, const DequantRegs& k) {
+  const uint32_t t = w >> 8;
+  const half2_t p0 = as_half2((w & k.lo) | k.magic);
+  const half2_t p1 = as_half2((w & k.hi) | k.magic);
+  const half2_t p2 = as_half2((t & k.lo) | k.magic);
+  const half2_t p3 = as_half2((t & k.hi) | k.magic);
+  half4_t lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  half4_t hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 }  // namespace q4

@@ -45,6 +45,9 @@ struct GemmArgs {
   int rows_per_wave;    // row tiles of 16 per wavefront: 1, 2 or 4
   int waves_per_group;  // wavefronts per workgroup splitting the channels: 1..16
   int col_tiles;        // 16-column batch tiles per wavefront: 1, 2 or 4
+  int k_splits;         // workgroups splitting the channels (B <= 16 path); > 1 needs workspace
+  void* workspace;      // float32 [k_splits][B][N] partial sums when k_splits > 1
+  int grid_limit;       // B <= 16: cap on the persistent grid (0 = as many as are resident)
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

@@ -140,12 +140,28 @@ def _prep_gemm(x, qw: QuantizedWeight, out):
     return B, out
 
 
+def _workspace(x, need: int, workspace):
+    """The caller's workspace tensor, or a fresh one when the shape needs it and none was given."""
+    import torch
+
+    if need == 0 and workspace is None:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    elif workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def gemm(x, qw: QuantizedWeight, out=None, workspace=None):
-    """q4_gemm / q4_gemm_asym: y = x . W_hat^T, float16 [B, out_features]."""
+    """q4_gemm / q4_gemm_asym: y = x . W_hat^T, float16 [B, out_features].
+
+    `workspace`: optional device tensor of at least workspace_bytes(B, out, in, group)
+    bytes (allocated here when needed and not given)."""
     B, out = _prep_gemm(x, qw, out)
     lib = _lib.load()
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    need = int(lib.q4_workspace_bytes(B, qw.out_features, qw.in_features, qw.group)) if B > 0 else 0
+    ws_ptr, ws_bytes = _workspace(x, need, workspace)
     if qw.asym:
         st = lib.q4_gemm_asym(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.zeros.data_ptr(),
                               qw.out_features, qw.in_features, qw.group, out.data_ptr(), ws_ptr, ws_bytes,
@@ -157,14 +173,17 @@ def gemm(x, qw: QuantizedWeight, out=None, workspace=None):
     return out
 
 
-def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int, out=None):
+def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int, k_splits: int = 1,
+                out=None, workspace=None):
     """q4_gemm_config: q4_gemm with an explicit launch shape (tuning)."""
     B, out = _prep_gemm(x, qw, out)
     lib = _lib.load()
+    need = 4 * k_splits * B * qw.out_features if (k_splits > 1 and B <= 16) else 0
+    ws_ptr, ws_bytes = _workspace(x, need, workspace)
     st = lib.q4_gemm_config(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(),
                             qw.zeros.data_ptr() if qw.zeros is not None else None, int(qw.asym),
                             qw.out_features, qw.in_features, qw.group, out.data_ptr(), rows_per_wave,
-                            waves_per_group, _stream(x))
+                            waves_per_group, k_splits, ws_ptr, ws_bytes, _stream(x))
     _check(st)
     return out
 
