@@ -8,14 +8,21 @@ the algorithmic bytes: packed codes + float16 scales + float16 activations
 (outputs not counted). Inputs are synthetic and already resident in HBM.
 
 The same line carries:
-  roofline      the dominant kernel (gate/up GEMV) against the 8 TB/s HBM peak,
-                its average duration measured with HIP events on its stream;
-  cpu_baseline  the CPU oracle timed on a bounded sample (layer 0), on this host;
-  extras        us/layer vs B (1, 2, 4, 8), the Llama-3-8B sweep, the batch sweep
-                on one 28672x8192 matrix with a dense bf16 torch.matmul beside it,
-                and quantize+pack throughput on the heavy-tailed 14336x4096 weights.
+  roofline      the dominant kernel (the fused gate/up GEMV, 55% of the bytes)
+                against the 8 TB/s HBM peak; its average duration is measured
+                with HIP events on its stream inside this run. `traffic` comes
+                from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary under profiles/
+                when that was taken on the current kernel sources, else null.
+  cpu_baseline  the CPU oracle (numpy float64) timed on a bounded sample of the
+                same sweep on this host.
+  extras        us/layer vs B (1, 2, 4, 8); the Llama-3-8B sweep; one 4096x4096
+                layer; the batch sweep on one 28672x8192 matrix with MFMA
+                utilisation and a dense bf16 torch.mm beside it; quantize+pack
+                throughput and the B = 1 GEMV on heavy-tailed 14336x4096 weights.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+Profiling helpers: --only-kernel {gate_up,down,qkv,o} [--reps N] runs just that
+GEMV kind of a few 70B layers; --copy-calibration runs a 256 MiB device copy.
 """
 
 from __future__ import annotations
@@ -31,14 +38,42 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "W4A16 GEMV effective HBM GB/s & % of peak (B=1); us/layer vs B"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_gate_up_70b_b1_traffic.txt")
+KIND_OF = {"q_proj+k_proj+v_proj": "qkv", "o_proj": "o", "gate_proj+up_proj": "gate_up", "down_proj": "down"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_sweep(shapes: dict, layers: int, seed: int, group: int, device):
-    """Quantize every layer's fused matrices on the GPU; returns [(name, N, K, qw)] per layer."""
+def events():
+    import torch
+
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def graph_time(fn, reps: int = 3) -> float:
+    """Seconds per replay of a HIP graph holding the launches `fn` makes."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = events()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / reps
+
+
+def build_model(shapes: dict, layers: int, seed: int, group: int, device):
+    """Quantize every layer's fused matrices on the GPU; returns [[(name, qw)]] per layer."""
     import torch
 
     import synth
@@ -53,8 +88,7 @@ def build_sweep(shapes: dict, layers: int, seed: int, group: int, device):
                      for n in grp]
             W = parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
             del parts
-            qw = q4.quantize_pack(W, group)
-            mats.append(("+".join(grp), W.shape[0], W.shape[1], qw))
+            mats.append(("+".join(grp), q4.quantize_pack(W, group)))
             del W
         model.append(mats)
     torch.cuda.synchronize()
@@ -68,15 +102,14 @@ class Sweep:
         import torch
 
         import synth
-
         import w4a16_decode_amd as q4
 
-        self.model = model
-        self.B = B
+        self.model, self.B = model, B
         self.xs, self.ys = [], []
         ws = 0
         for layer, mats in enumerate(model):
-            for i, (_, N, K, qw) in enumerate(mats):
+            for i, (_, qw) in enumerate(mats):
+                K, N = qw.in_features, qw.out_features
                 self.xs.append(synth.device_activation(B, K, seed=seed, layer=layer, matrix=100 + i, device=device))
                 self.ys.append(torch.empty((B, N), dtype=torch.float16, device=device))
                 ws = max(ws, q4.workspace_bytes(B, N, K, qw.group))
@@ -87,7 +120,7 @@ class Sweep:
     def launches(self):
         i = 0
         for mats in self.model:
-            for (name, N, K, qw) in mats:
+            for name, qw in mats:
                 yield name, self.xs[i], qw, self.ys[i]
                 i += 1
 
@@ -121,8 +154,7 @@ class Sweep:
         for _ in range(warmup):
             self.graph.replay()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
+        t0, t1 = events()
         t0.record()
         for _ in range(steps):
             self.graph.replay()
@@ -142,8 +174,7 @@ class Sweep:
             evs = []
             for name, x, qw, y in self.launches():
                 if name == pick:
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
+                    a, b = events()
                     a.record(stream)
                     q4.gemm(x, qw, out=y, workspace=self.ws)
                     b.record(stream)
@@ -155,9 +186,117 @@ class Sweep:
         return durs
 
 
-def cpu_baseline(layers_W, B: int, group: int) -> dict:
-    """Oracle (numpy) W4A16 product on a bounded sample, timed on this host's cores."""
+def recorded_traffic():
+    """Traffic per launch from profiles/, only if taken on the current kernel sources."""
+    from w4a16_decode_amd import profiling
+
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_fingerprint") != profiling.kernel_fingerprint():
+        return None
+    try:
+        return float(vals["bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
+    """28672x8192: W4A16 at B in {1,4,16,32,64,128,256} vs dense bf16 torch.mm."""
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+    from w4a16_decode_amd import perfmodel
+
+    N, K = 28672, 8192
+    copies = 10  # 10 x 121 MB rotate past the 256 MB last-level cache
+    qws = []
+    for c in range(copies):
+        W = synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev)
+        qws.append(q4.quantize_pack(W, group))
+        del W
+    dense = []
+    for c in range(3):  # 3 x 470 MB bf16, stored [K, N] so torch.mm needs no transpose
+        dense.append(synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev).to(torch.bfloat16).t().contiguous())
+    out = {}
+    for B in (1, 4, 16, 32, 64, 128, 256):
+        x = synth.device_activation(B, K, seed=4, layer=0, matrix=0, device=dev)
+        y = torch.empty((B, N), dtype=torch.float16, device=dev)
+        ws = torch.empty(max(16, q4.workspace_bytes(B, N, K, group)), dtype=torch.uint8, device=dev)
+        t = graph_time(lambda: [q4.gemm(x, qw, out=y, workspace=ws) for qw in qws]) / copies
+        xb = x.to(torch.bfloat16)
+        for Wd in dense:
+            torch.mm(xb, Wd)
+        torch.cuda.synchronize()
+        a, b = events()
+        a.record()
+        reps = 4
+        for _ in range(reps):
+            for Wd in dense:
+                torch.mm(xb, Wd)
+        b.record()
+        torch.cuda.synchronize()
+        td = a.elapsed_time(b) / 1e3 / (reps * len(dense))
+        flops = perfmodel.gemm_flops(B, N, K)
+        nbytes = perfmodel.gemm_read_bytes(B, N, K, group)
+        out[str(B)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                       "TFLOPs": round(flops / t / 1e12, 2),
+                       "mfma_util": round(flops / t / 1e12 / perfmodel.MFMA_FP16_DENSE_TFLOPS, 4),
+                       "bf16_dense_us": round(td * 1e6, 2), "speedup_vs_bf16": round(td / t, 3)}
+        log(f"{log_prefix} 28672x8192 B={B}: {t * 1e6:.1f} us ({nbytes / t / 1e9:.0f} GB/s, "
+            f"{flops / t / 1e12:.1f} TFLOP/s) vs bf16 mm {td * 1e6:.1f} us")
+    crossover = next((int(b) for b, v in out.items() if v["speedup_vs_bf16"] < 1.0), None)
+    return {"per_B": out, "first_B_slower_than_bf16": crossover}
+
+
+def extras_quantize(dev):
+    """Heavy-tailed 14336x4096: quantize+pack throughput and the B = 1 GEMV, g in {32, 64, 128}."""
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+    from w4a16_decode_amd import perfmodel
+
+    N, K = 14336, 4096
+    Wh, _ = synth.heavy_tailed_weight(N, K, seed=5)
+    base = torch.from_numpy(Wh).to(dev)
+    Ws = [base] + [base.clone() for _ in range(7)]  # 8 x 117 MB rotate past the last-level cache
+    x = synth.device_activation(1, K, seed=5, layer=0, matrix=0, device=dev)
+    y = torch.empty((1, N), dtype=torch.float16, device=dev)
+    out = {}
+    for g in (32, 64, 128):
+        for asym in (False, True):
+            qws = [q4.quantize_pack(W, g, asym=asym) for W in Ws]
+            torch.cuda.synchronize()
+            a, b = events()
+            a.record()
+            reps = 3
+            for _ in range(reps):
+                for W in Ws:
+                    q4.quantize_pack(W, g, asym=asym)
+            b.record()
+            torch.cuda.synchronize()
+            tq = a.elapsed_time(b) / 1e3 / (reps * len(Ws))
+            ws = torch.empty(max(16, q4.workspace_bytes(1, N, K, g)), dtype=torch.uint8, device=dev)
+            tg = graph_time(lambda: [q4.gemm(x, qw, out=y, workspace=ws) for qw in qws]) / len(qws)
+            qb = perfmodel.quantize_bytes(N, K, g, asym)
+            gb = perfmodel.gemm_read_bytes(1, N, K, g, asym)
+            out[f"g{g}_{'asym' if asym else 'sym'}"] = {
+                "quantize_us": round(tq * 1e6, 2), "quantize_GBps": round(qb / tq / 1e9, 1),
+                "gemv_us": round(tg * 1e6, 2), "gemv_GBps": round(gb / tg / 1e9, 1)}
+            del qws
+    return out
+
+
+def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) -> dict:
+    """Oracle (numpy) W4A16 product on whole layers of the 70B sweep, until ~target_s of CPU time."""
     import numpy as np
+    import torch
 
     import oracle
     import synth
@@ -169,17 +308,53 @@ def cpu_baseline(layers_W, B: int, group: int) -> dict:
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    total_bytes = 0
-    t_total = 0.0
-    for (N, K, W) in layers_W:
-        x = synth.activation(B, K, seed=11)
-        q, s = oracle.quantize_sym(W, group)            # setup, not timed
-        t0 = time.perf_counter()
-        y = oracle.gemm_ref(x, oracle.dequant_sym(q, s, group))
-        t_total += time.perf_counter() - t0
-        assert y.shape == (B, N) and np.all(np.isfinite(y))
-        total_bytes += perfmodel.gemm_read_bytes(B, N, K, group)
-    return {"seconds": t_total, "bytes": total_bytes, "threads": threads}
+    order = {name: i for i, name in enumerate(synth.MATRIX_ORDER)}
+    total_bytes, t_total, layers = 0, 0.0, 0
+    while t_total < target_s and layers < max_layers:
+        for grp in synth.FUSED_GROUPS:
+            parts = [synth.device_weight(*synth.LLAMA3_70B[n], seed=3, layer=layers, matrix=order[n], device=dev)
+                     for n in grp]
+            W = (torch.cat(parts, 0) if len(parts) > 1 else parts[0]).cpu().numpy()
+            del parts
+            N, K = W.shape
+            x = synth.activation(1, K, seed=11, layer=layers)
+            q, s = oracle.quantize_sym(W, group)  # setup, not timed
+            del W
+            t0 = time.perf_counter()
+            yy = oracle.gemm_ref(x, oracle.dequant_sym(q, s, group))
+            t_total += time.perf_counter() - t0
+            assert yy.shape == (1, N) and np.all(np.isfinite(yy))
+            total_bytes += perfmodel.gemm_read_bytes(1, N, K, group)
+        layers += 1
+    return {"seconds": t_total, "bytes": total_bytes, "threads": threads, "layers": layers}
+
+
+def only_kernel(kind: str, reps: int, layers: int, dev, group: int):
+    """Run just one GEMV kind of a few 70B layers, for counter collection."""
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+
+    model = build_model(synth.LLAMA3_70B, layers, seed=3, group=group, device=dev)
+    sweep = Sweep(model, 1, seed=3, device=dev)
+    picked = [(x, qw, y) for name, x, qw, y in sweep.launches() if KIND_OF[name] == kind]
+    for _ in range(reps):
+        for x, qw, y in picked:
+            q4.gemm(x, qw, out=y, workspace=sweep.ws)
+    torch.cuda.synchronize()
+    log(f"[bench] ran {kind} x {reps * len(picked)}")
+
+
+def copy_calibration(dev):
+    import torch
+
+    a = torch.ones(128 * 1024 * 1024, dtype=torch.float16, device=dev)  # 256 MiB
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("[bench] copied 3 x 256 MiB (268435456 bytes read and written per copy)")
 
 
 def main(argv=None):
@@ -190,11 +365,14 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=80)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only-kernel", choices=["gate_up", "down", "qkv", "o"])
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the kernel shards by output rows, see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build has no "
+              "multi-GPU path (the GEMV would shard by output rows, see the design notes)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -207,12 +385,18 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     group = 128
-    log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return 0
+    if args.only_kernel:
+        only_kernel(args.only_kernel, args.reps, min(args.layers, 4), dev, group)
+        return 0
 
+    log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")
     t_setup = time.perf_counter()
-    model = build_sweep(synth.LLAMA3_70B, args.layers, seed=3, group=group, device=dev)
+    model = build_model(synth.LLAMA3_70B, args.layers, seed=3, group=group, device=dev)
     log(f"[bench] quantized {args.layers} layers in {time.perf_counter() - t_setup:.1f}s, "
-        f"{sum(qw.nbytes() for m in model for *_, qw in m) / 1e9:.2f} GB resident")
+        f"{sum(qw.nbytes() for m in model for _, qw in m) / 1e9:.2f} GB resident")
 
     sweep = Sweep(model, 1, seed=3, device=dev)
     sweep.capture()
@@ -221,17 +405,19 @@ def main(argv=None):
     gbs = bytes_step / step_s / 1e9
     log(f"[bench] B=1 sweep: {step_s * 1e3:.3f} ms/step, {gbs:.1f} GB/s ({gbs / perfmodel.HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
-    # dominant kernel: the fused gate/up GEMV (55% of the bytes)
+    # dominant kernel: the fused gate/up GEMV (55% of the bytes), HIP events on its stream
     durs = sweep.time_kernel("gate_proj+up_proj")
     d_avg = float(np.mean([d for d, _ in durs]))
     qw0 = durs[0][1]
     kbytes = perfmodel.gemm_read_bytes(1, qw0.out_features, qw0.in_features, group)
     k_gbs = kbytes / d_avg / 1e9
     log(f"[bench] gate/up GEMV {qw0.out_features}x{qw0.in_features}: {d_avg * 1e6:.2f} us, {k_gbs:.1f} GB/s")
+    traffic = recorded_traffic()
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / perfmodel.HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": f"gemm_kernel gate/up {qw0.out_features}x{qw0.in_features} B=1",
-                "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes}
+                "frac": round(k_gbs / perfmodel.HBM_PEAK_GBS, 4),
+                "traffic": round(traffic) if traffic is not None else None,
+                "kernel": f"gemv_kernel, fused gate/up {qw0.out_features}x{qw0.in_features}, B=1, g=128",
+                "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes, "launches_timed": len(durs)}
 
     extras = {}
     if not args.no_extras:
@@ -247,25 +433,46 @@ def main(argv=None):
                 del sw
         extras["us_per_layer_vs_B_70b"] = per_layer
         log(f"[bench] us/layer vs B: {per_layer}")
-    del sweep
+    del sweep, model
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        m8 = build_model(synth.LLAMA3_8B, 32, seed=2, group=group, device=dev)
+        s8 = Sweep(m8, 1, seed=2, device=dev)
+        s8.capture()
+        t8 = s8.time_steps(args.steps, args.warmup)
+        extras["sweep_8b_b1"] = {"ms_per_step": round(t8 * 1e3, 4), "GBps": round(s8.bytes_per_step() / t8 / 1e9, 1),
+                                 "us_per_layer": round(t8 / 32 * 1e6, 2)}
+        log(f"[bench] 8B sweep: {extras['sweep_8b_b1']}")
+        del s8, m8
+
+        W1 = synth.device_weight(4096, 4096, seed=0, layer=0, matrix=0, device=dev)
+        qws = [q4.quantize_pack(W1, group)] + [q4.quantize_pack(synth.device_weight(4096, 4096, seed=0, layer=c,
+                                                                                  matrix=0, device=dev), group)
+                                              for c in range(1, 128)]
+        x1 = synth.device_activation(1, 4096, seed=0, layer=0, matrix=0, device=dev)
+        y1 = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+        t1 = graph_time(lambda: [q4.gemm(x1, qw, out=y1) for qw in qws]) / len(qws)
+        b1 = perfmodel.gemm_read_bytes(1, 4096, 4096, group)
+        extras["single_layer_4096_b1"] = {"us": round(t1 * 1e6, 3), "GBps": round(b1 / t1 / 1e9, 1)}
+        log(f"[bench] 4096x4096 B=1: {extras['single_layer_4096_b1']}")
+        del qws, W1
+        torch.cuda.empty_cache()
+
+        extras["batch_sweep_28672x8192"] = extras_batch_sweep(dev, group)
+        torch.cuda.empty_cache()
+        extras["heavy_tailed_14336x4096"] = extras_quantize(dev)
+        log(f"[bench] heavy-tailed: {extras['heavy_tailed_14336x4096']}")
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
-        # bounded sample: layer 0 of the sweep, regenerated on the GPU and copied to the host
-        order = {name: i for i, name in enumerate(synth.MATRIX_ORDER)}
-        sample = []
-        for grp in synth.FUSED_GROUPS:
-            parts = [synth.device_weight(*synth.LLAMA3_70B[n], seed=3, layer=0, matrix=order[n], device=dev)
-                     for n in grp]
-            W = torch.cat(parts, 0) if len(parts) > 1 else parts[0]
-            sample.append((W.shape[0], W.shape[1], W.cpu().numpy()))
-            del W, parts
-        res = cpu_baseline(sample, 1, group)
+        res = cpu_baseline(dev, group)
         cpu_gbs = res["bytes"] / res["seconds"] / 1e9
         cpu = {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": res["threads"], "kind": "oracle",
-               "sample": "layer 0 of the 70B sweep (q/k/v, o, gate/up, down), B=1: float64 dequantize + "
-                         f"numpy matmul, {res['seconds']:.1f} s"}
-        log(f"[bench] cpu oracle: {cpu_gbs:.3f} GB/s over {res['seconds']:.1f}s")
+               "sample": f"the first {res['layers']} layers of the 70B sweep (q/k/v, o, gate/up, down), B=1: "
+                         f"float64 dequantize + numpy matmul, {res['seconds']:.1f} s of oracle time"}
+        log(f"[bench] cpu oracle: {cpu_gbs:.3f} GB/s over {res['seconds']:.1f}s ({res['layers']} layers)")
 
     out = {
         "metric": METRIC,

@@ -90,20 +90,21 @@ size_t lds_per_block() {
 }
 
 // LDS of one GEMV workgroup holding one row block (q4_gemm.hip, GemvLds): x slice
-// + zero row, the per-unit biases of symmetric codes (sized for g = 32, the most
-// units), two reduction buffers and the result buffer of one row block. The launch
-// adds result space for further row blocks only within a fixed 16 KiB.
-size_t gemv_lds(int B, int S, int KS, int W, int R) {
+// + zero row, the per-unit biases of symmetric codes, two reduction buffers and
+// the results of one row block. The launch keeps further row blocks' results in
+// what is left of the limit.
+size_t gemv_lds(int B, int S, int KS, int W, int R, int group, bool asym) {
   const size_t nsb = (size_t)((S + KS - 1) / KS);
+  const size_t gsub = group >= 128 ? 1 : (size_t)(128 / group);
   const size_t x = (((size_t)B * (nsb * 128 + 8) + 128) * 2 + 15) & ~(size_t)15;
-  const size_t beta = ((size_t)B * nsb * 4 + 1 + 3) / 4 * 4 * sizeof(float);
-  return x + beta + 2 * (size_t)W * R * 1024 + 16 * 1024;
+  const size_t beta = asym ? 0 : ((size_t)B * nsb * gsub + 1 + 3) / 4 * 4 * sizeof(float);
+  return x + beta + 2 * (size_t)W * R * 1024 + (size_t)R * 16 * B * 4;
 }
 
-bool gemv_shape_ok(int B, int S, int KS, int W, int R, size_t lds_limit) {
+bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, size_t lds_limit) {
   if (KS < 1 || KS > S || W < 1 || W > 8 || W > S / KS) return false;
   const int nsb = (S + KS - 1) / KS;
-  if (gemv_lds(B, S, KS, W, R) > lds_limit) return false;
+  if (gemv_lds(B, S, KS, W, R, group, asym) > lds_limit) return false;
   return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
 }
 
@@ -115,10 +116,13 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     // at most half of a 160 KiB CU, so two 8-wavefront workgroups stay resident
     const size_t lim = std::min<size_t>(lds_per_block(), 80 * 1024);
     a->col_tiles = 1;
-    int R = T >= 2048 ? 2 : 1;
+    // one row tile per wavefront for tall matrices and small groups (several scales
+    // per block), two when there are fewer than 2048 tiles (fewer, longer-lived
+    // workgroups amortise the start-up better)
+    int R = (T >= 2048 || d.group < 128) ? 1 : 2;
     int W = std::min(8, S);
     int KS = 1;
-    while (!gemv_shape_ok(B, S, KS, W, R, lim)) {
+    while (!gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim)) {
       if (R > 1) { R = 1; continue; }
       if (KS < S && W <= S / (KS + 1)) { ++KS; continue; }
       if (W > 1) { W /= 2; KS = 1; continue; }
@@ -127,6 +131,7 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     a->rows_per_wave = R;
     a->waves_per_group = W;
     a->k_splits = KS;
+    a->lds_limit = lim;
     return;
   }
   a->col_tiles = col_tiles_total == 2 ? 2 : 4;
@@ -249,7 +254,8 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
     if (waves_per_group < 1 || waves_per_group > 8)
       return fail(Q4_ERR_UNSUPPORTED, "waves_per_group must be in [1, 8]");
     if (B <= 16) {
-      if (!gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, lds_per_block()))
+      a.lds_limit = lds_per_block();
+      if (!gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, asym, a.lds_limit))
         return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: the activation slice of B=%lld and "
                     "the reduction buffers exceed LDS, or fewer than one 128-channel block per wavefront",
                     (int)k_splits, (int)waves_per_group, (long long)B);

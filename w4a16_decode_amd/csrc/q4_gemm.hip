@@ -219,8 +219,19 @@ struct GemvLds {
   }
 };
 
+#ifndef Q4_GEMV_WAVES_R1
+#define Q4_GEMV_WAVES_R1 4
+#endif
+#ifndef Q4_GEMV_WAVES_R2
+#define Q4_GEMV_WAVES_R2 4
+#endif
+// Register budget for one group per block (g >= 128): at least Q4_GEMV_WAVES_R*
+// wavefronts per SIMD (512 / waves VGPRs). Smaller groups keep more scales per
+// block and run without a budget rather than spill.
 template <int R, int GSUB, bool ASYM, int P, bool NTL>
-__global__ __launch_bounds__(512) void gemv_kernel(const uint16_t* __restrict__ x, int B,
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu((GSUB > 1 || R > 2) ? 1 : (R == 1 ? Q4_GEMV_WAVES_R1 : Q4_GEMV_WAVES_R2), 8)))
+void gemv_kernel(const uint16_t* __restrict__ x, int B,
                                                    const uint4* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, int N, int K, int T, int S,
@@ -530,7 +541,7 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
 #define Q4_GEMV_DEPTH_R1 8
 #endif
 #ifndef Q4_GEMV_DEPTH_R2
-#define Q4_GEMV_DEPTH_R2 6
+#define Q4_GEMV_DEPTH_R2 4
 #endif
   // pipeline depth (blocks of codes in flight + 1) per row-tile count; fixed at
   // build time (the macros exist so tuning builds can try other depths)
@@ -551,7 +562,10 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, lds1) * device_cus();
   const int64_t units = (int64_t)nRB * KS;
   int64_t rounds = (units + resident - 1) / resident;
-  const int64_t max_rounds = std::max<int64_t>(1, (16 * 1024) / ((int64_t)R * 16 * a.B * 4));
+  // each further row block per workgroup adds its results to the LDS buffer
+  const size_t out1 = (size_t)R * 16 * a.B * 4;
+  const size_t lim = a.lds_limit > lds1 ? a.lds_limit : lds1;
+  const int64_t max_rounds = std::max<int64_t>(1, (int64_t)((lim - lds1) / out1) + 1);
   rounds = std::min(rounds, max_rounds);
   int64_t per_split = ((int64_t)nRB + rounds - 1) / rounds;
   if (a.grid_limit > 0) per_split = std::min<int64_t>(per_split, std::max(1, a.grid_limit / KS));

@@ -48,6 +48,7 @@ struct GemmArgs {
   int k_splits;         // workgroups splitting the channels (B <= 16 path); > 1 needs workspace
   void* workspace;      // float32 [k_splits][B][N] partial sums when k_splits > 1
   int grid_limit;       // B <= 16: cap on the persistent grid (0 = as many as are resident)
+  size_t lds_limit;     // B <= 16: LDS a workgroup may use (sizes the per-workgroup result buffer)
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
