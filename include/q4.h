@@ -139,17 +139,22 @@ q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void*
                        const void* zeros, int64_t out, int64_t in, int32_t group, void* y,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* q4_gemm with an explicit launch shape, for tuning: `rows_per_wave` row tiles
- * of 16 per wavefront (1, 2 or 4), `waves_per_group` wavefronts per workgroup
- * (1..8) splitting the channel range, `k_splits` workgroups splitting it further
- * (B <= 16 only; 1 otherwise). Needs k_splits * B * out * 4 bytes of workspace
- * when k_splits > 1. Returns Q4_ERR_UNSUPPORTED for shapes the kernels cannot
- * run (e.g. an activation slice larger than the 64 KiB LDS budget). `asym`
- * selects q4_gemm_asym semantics (zeros used). */
+/* q4_gemm with an explicit launch shape, for tuning. `asym` selects q4_gemm_asym
+ * semantics (zeros used). Returns Q4_ERR_UNSUPPORTED for shapes the kernels
+ * cannot run.
+ * B <= 16 (GEMV): `rows_per_wave` row tiles of 16 per wavefront (1, 2 or 4),
+ *   `waves_per_group` wavefronts per workgroup (1..8) splitting the channel range,
+ *   `k_splits` workgroups splitting it further, `col_tiles` must be 1. The
+ *   activation slice of one split must fit the device's LDS per workgroup. Needs
+ *   k_splits * B * out * 4 bytes of workspace when k_splits > 1.
+ * B > 16 (skinny GEMM): `rows_per_wave` 1, 2 or 4, `waves_per_group` 4,
+ *   `k_splits` 1, `col_tiles` 2, 4 or 8 tiles of 16 batch rows per workgroup,
+ *   with rows_per_wave * col_tiles * max(1, 128 / group) <= 16 (accumulator
+ *   registers); no workspace. */
 q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales,
                          const void* zeros, int32_t asym, int64_t out, int64_t in, int32_t group,
                          void* y, int32_t rows_per_wave, int32_t waves_per_group, int32_t k_splits,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int32_t col_tiles, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device layout -> canonical layout (see above). `zeros`/`canon_zeros` are used
  * only when asym != 0. canon_codes: out*in/2 bytes; canon_scales: out*(in/group)

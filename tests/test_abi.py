@@ -93,17 +93,21 @@ def test_gemm_validation(lib):
     assert g(FAKE, 1, FAKE, FAKE, 16, 128, 128, FAKE + 1, None, 0, None) == 4
     assert lib.q4_gemm_asym(FAKE, 1, FAKE, FAKE, None, 16, 128, 128, FAKE, None, 0, None) == 1
     c = lib.q4_gemm_config
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 3, 1, 1, None, 0, None) == 5
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 9, 1, None, 0, None) == 5
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 0, 0, 0, None, 0, None) == 5
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 8, 3, None, 0, None) == 5   # k_splits > blocks
-    assert c(FAKE, 16, FAKE, FAKE, None, 0, 16, 8192, 128, FAKE, 1, 8, 1, None, 0, None) == 5  # x slice > LDS
-    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 8, 1, None, 0, None) == 5   # B > 16, R*NT > 4
-    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 8, 2, None, 0, None) == 5   # k_splits, B > 16
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 3, 1, 1, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 9, 1, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 0, 0, 0, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 8, 3, 1, None, 0, None) == 5   # k_splits > blocks
+    assert c(FAKE, 16, FAKE, FAKE, None, 0, 16, 8192, 128, FAKE, 1, 8, 1, 1, None, 0, None) == 5  # x slice > LDS
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 8, 1, 4, None, 0, None) == 5   # B > 16: 4 wavefronts
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 8, 2, 4, None, 0, None) == 5   # k_splits, B > 16
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 4, 1, 8, None, 0, None) == 5   # R*CT > 16
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 32, FAKE, 2, 4, 1, 4, None, 0, None) == 5    # R*CT*4 > 16
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 4, 1, 3, None, 0, None) == 5   # col_tiles
+    assert c(FAKE, 4, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 1, 1, 2, None, 0, None) == 5    # GEMV: 1 tile
     # split k needs workspace: 2 * 1 * 16 * 4 bytes here
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, None, 0, None) == 6
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, FAKE, 64, None) == 6
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, FAKE + 4, 128, None) == 4
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, 1, None, 0, None) == 6
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, 1, FAKE, 64, None) == 6
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, 1, FAKE + 4, 128, None) == 4
 
 
 def test_workspace_sizes(lib):

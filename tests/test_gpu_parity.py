@@ -122,6 +122,7 @@ GEMM_CASES = [  # (B, N, K, g, asym)
     (9, 64, 2048, 128, False), (15, 47, 1024, 128, False), (16, 200, 1024, 128, True), (17, 100, 512, 128, False),
     (31, 48, 1024, 64, False), (33, 65, 768, 128, True), (64, 128, 2048, 128, False), (65, 40, 512, 32, False),
     (100, 300, 1024, 128, False), (256, 96, 1024, 128, True), (1, 16, 4096, 4096, False), (2, 4000, 256, 128, False),
+    (48, 40, 4096, 4096, False), (20, 33, 1024, 512, True), (129, 17, 384, 64, True),
 ]
 
 
@@ -160,6 +161,35 @@ def test_gemm_launch_shapes_agree(q4):
                 assert_close(y1, ref, f"R={R} W={Wv} KS={KS}")
                 ran += 1
     assert ran >= 20
+
+
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
+@pytest.mark.parametrize("B,g", [(40, 128), (100, 32), (200, 64)])
+def test_gemm_mfma_shapes_agree(q4, B, g, asym):
+    """Skinny GEMM (B > 16): every row-tile / column-tile shape the kernel builds
+    meets the tolerance and is deterministic; ragged rows (N = 300), a ragged last
+    column group and a channel count that is not a multiple of the prefetch depth."""
+    N, K = 300, 1280
+    W = synth.weight(N, K, seed=B)
+    x = synth.activation(B, K, seed=B + 1)
+    qw, q_o, s_o, z_o = _check_quant_exact(q4, W, g, asym, device_layout=False)
+    ref = _ref_product(x, q_o, s_o, z_o, g)
+    xg = to_gpu(x)
+    gsub = max(1, 128 // g)
+    ran = 0
+    for R in (1, 2, 4):
+        for CT in (2, 4, 8):
+            say(f"  config B={B} g={g} R={R} CT={CT}")
+            try:
+                y1 = to_np(q4.gemm_config(xg, qw, R, 4, 1, col_tiles=CT))
+            except q4.Q4Error as e:
+                assert e.status == 5 and R * CT * gsub > 16, str(e)
+                continue
+            y2 = to_np(q4.gemm_config(xg, qw, R, 4, 1, col_tiles=CT))
+            assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "non-deterministic"
+            assert_close(y1, ref, f"B={B} g={g} R={R} CT={CT}")
+            ran += 1
+    assert ran >= 3
 
 
 def test_gemm_empty_batch(q4):

@@ -108,6 +108,20 @@ bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, siz
   return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
 }
 
+// LDS of one skinny-GEMM workgroup: two activation tiles of col_tiles * 16 rows x
+// 136 halfs (128 channels + a 16-byte pad against bank conflicts).
+size_t mfma_lds(int col_tiles) { return (size_t)2 * col_tiles * 16 * 136 * 2; }
+
+// Register budget of the skinny GEMM: R x CT accumulator tiles and one partial tile
+// per group of a 128-channel block.
+bool mfma_shape_ok(int R, int W, int KS, int CT, int group) {
+  if (W != 4 || KS != 1) return false;
+  if (R != 1 && R != 2 && R != 4) return false;
+  if (CT != 2 && CT != 4 && CT != 8) return false;
+  const int gsub = group >= 128 ? 1 : 128 / group;
+  return R * CT * gsub <= 16 && mfma_lds(CT) <= lds_per_block();
+}
+
 void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
   const int T = d.Np / 16;
   const int S = d.Kp / 128;
@@ -134,16 +148,18 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     a->lds_limit = lim;
     return;
   }
-  a->col_tiles = col_tiles_total == 2 ? 2 : 4;
-  const int col_groups = (col_tiles_total + a->col_tiles - 1) / a->col_tiles;
-  int R = (T >= 512) ? 2 : 1;
-  if (a->col_tiles == 4) R = 1;
-  const int64_t wgs = (int64_t)((T + R - 1) / R) * col_groups;
-  int W = 1;
-  while (W < 8 && wgs * W < 4096 && S / (2 * W) >= 1) W *= 2;
-  while (W > 1 && (int64_t)W * R * a->col_tiles * 1024 > (int64_t)kLdsFallback) W /= 2;
+  // B > 16: skinny MFMA GEMM, 4 wavefronts per workgroup, CT column tiles of 16
+  // per workgroup (double-buffered activation tile in LDS), R row tiles per wavefront
+  int CT = col_tiles_total <= 2 ? 2 : (col_tiles_total <= 4 ? 4 : 8);
+  int R = (B <= 64 || T < 1024) ? 1 : 2;
+  while (!mfma_shape_ok(R, 4, 1, CT, d.group)) {
+    if (R > 1) R /= 2;
+    else if (CT > 2) CT /= 2;
+    else break;  // unreachable: R = 1, CT = 2 always fits
+  }
+  a->col_tiles = CT;
   a->rows_per_wave = R;
-  a->waves_per_group = W;
+  a->waves_per_group = 4;
   a->k_splits = 1;
 }
 
@@ -220,8 +236,8 @@ q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t 
 
 static q4_status gemm_common(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                              bool asym, int64_t out, int64_t in, int32_t group, void* y, int rows_per_wave,
-                             int waves_per_group, int k_splits, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             int waves_per_group, int k_splits, int col_tiles, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (B < 0 || B >= kMaxDim) return fail(Q4_ERR_SHAPE, "B=%lld out of range", (long long)B);
   Dims d;
   q4_status st = check_dims(out, in, group, &d);
@@ -248,24 +264,23 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
   a.Gp = d.Gp;
   a.y = y;
   pick_shape((int)B, d, &a);
-  if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0) {
+  if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0 || col_tiles > 0) {
     if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
       return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave must be 1, 2 or 4");
     if (waves_per_group < 1 || waves_per_group > 8)
       return fail(Q4_ERR_UNSUPPORTED, "waves_per_group must be in [1, 8]");
     if (B <= 16) {
+      if (col_tiles != 1) return fail(Q4_ERR_UNSUPPORTED, "col_tiles must be 1 for B <= 16");
       a.lds_limit = lds_per_block();
       if (!gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, asym, a.lds_limit))
         return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: the activation slice of B=%lld and "
                     "the reduction buffers exceed LDS, or fewer than one 128-channel block per wavefront",
                     (int)k_splits, (int)waves_per_group, (long long)B);
-    } else {
-      if (k_splits != 1) return fail(Q4_ERR_UNSUPPORTED, "k_splits must be 1 for B > 16");
-      if (rows_per_wave * a.col_tiles > 4)
-        return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave * column tiles must be <= 4 for B > 16");
-      if ((int64_t)waves_per_group * rows_per_wave * a.col_tiles * 1024 > (int64_t)kLdsFallback)
-        return fail(Q4_ERR_UNSUPPORTED, "waves_per_group * rows_per_wave * column tiles exceeds the reduction buffer");
+    } else if (!mfma_shape_ok(rows_per_wave, waves_per_group, k_splits, col_tiles, d.group)) {
+      return fail(Q4_ERR_UNSUPPORTED, "for B > 16: waves_per_group must be 4, k_splits 1, col_tiles 2, 4 or 8 "
+                  "(within LDS), rows_per_wave * col_tiles * max(1, 128 / group) <= 16");
     }
+    a.col_tiles = col_tiles;
     a.rows_per_wave = rows_per_wave;
     a.waves_per_group = waves_per_group;
     a.k_splits = k_splits;
@@ -283,25 +298,25 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
 
 q4_status q4_gemm(const void* x, int64_t B, const void* packed, const void* scales, int64_t out, int64_t in,
                   int32_t group, void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, 0, workspace, workspace_bytes,
+  return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, 0, 0, workspace, workspace_bytes,
                      stream);
 }
 
 q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                        int64_t out, int64_t in, int32_t group, void* y, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return gemm_common(x, B, packed, scales, zeros, true, out, in, group, y, 0, 0, 0, workspace, workspace_bytes,
+  return gemm_common(x, B, packed, scales, zeros, true, out, in, group, y, 0, 0, 0, 0, workspace, workspace_bytes,
                      stream);
 }
 
 q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                          int32_t asym, int64_t out, int64_t in, int32_t group, void* y, int32_t rows_per_wave,
-                         int32_t waves_per_group, int32_t k_splits, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  if (rows_per_wave <= 0 || waves_per_group <= 0 || k_splits <= 0)
-    return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave, waves_per_group and k_splits must be positive");
+                         int32_t waves_per_group, int32_t k_splits, int32_t col_tiles, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (rows_per_wave <= 0 || waves_per_group <= 0 || k_splits <= 0 || col_tiles <= 0)
+    return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave, waves_per_group, k_splits and col_tiles must be positive");
   return gemm_common(x, B, packed, scales, zeros, asym != 0, out, in, group, y, rows_per_wave, waves_per_group,
-                     k_splits, workspace, workspace_bytes, stream);
+                     k_splits, col_tiles, workspace, workspace_bytes, stream);
 }
 
 q4_status q4_to_canonical(const void* packed, const void* scales, const void* zeros, int32_t asym, int64_t out,

@@ -15,10 +15,11 @@
 //  * Dequantization is exact in float16 (magic-number OR + one packed add/fma per
 //    pair, see dequant8), so the MFMA contracts the integer codes against float16 x
 //    with float32 accumulation; each group's partial is scaled in float32.
-//  * The batch (B <= 16) fills the 16 MFMA columns; larger B uses up to 4 column
-//    tiles per wavefront and more workgroups along y.
-//  * A workgroup owns R row tiles; its wavefronts split the channel range and the
-//    partial sums are reduced through LDS in a fixed order (deterministic).
+//  * The batch (B <= 16) fills the 16 MFMA columns of the GEMV; its wavefronts
+//    split the channel range and their partial sums are reduced through LDS in a
+//    fixed order (deterministic). Larger B runs the skinny GEMM: 2 to 8 column
+//    tiles of 16 batch rows per workgroup, staged through LDS and shared by its
+//    four wavefronts, each owning whole row tiles.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -36,152 +37,6 @@ __device__ __forceinline__ uint32_t lane_dword(const uint4& v, int m) {
 
 __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// Registers one pipeline stage holds: the codes of R row tiles for one 128-channel
-// block, the matching activation slices for NT column tiles, the scales (and zero
-// points) of the groups in the block.
-template <int R, int NT, int GSUB, bool ASYM>
-struct Stage {
-  uint4 w[R];
-  half8_t x[NT][4];
-  uint2 sc[R][GSUB];
-  uint32_t z[R][GSUB];
-};
-
-// GSUB: groups per 128-channel block (4: g = 32, 2: g = 64, 1: g = 128*J).
-// P: pipeline depth -- loads for P-1 blocks ahead are in flight while one is computed.
-template <int R, int NT, int GSUB, bool ASYM, int P>
-__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ x, int B,
-                                                   const uint4* __restrict__ packed,
-                                                   const uint16_t* __restrict__ scales,
-                                                   const uint8_t* __restrict__ zeros, int N, int K, int T, int S,
-                                                   int Gp, int J, uint16_t* __restrict__ y) {
-  extern __shared__ float red[];
-  constexpr int MPG = 4 / GSUB;  // 32-channel steps per group inside a block
-  const int W = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tile0 = blockIdx.x * R;
-  const int col0 = blockIdx.y * NT;
-  const int sb0 = (int)(((int64_t)S * wave) / W);
-  const int sb1 = (int)(((int64_t)S * (wave + 1)) / W);
-  const int kq = lane >> 4;          // 8-channel slice fed by this lane in each 32-channel step
-  const int crow = 4 * (lane >> 4);  // first of the 4 accumulator rows held by this lane
-  const int arow = lane & 15;        // A-operand row (weight row) held by this lane
-
-  int tiles[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) tiles[r] = min(tile0 + r, T - 1);  // clamped: loads stay in bounds
-
-  float4_t acc[R][NT];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int c = 0; c < NT; ++c) acc[r][c] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const half8_t zero8 = {};
-  const half2_t sym_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const half2_t sym_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-
-  auto load = [&](Stage<R, NT, GSUB, ASYM>& st, int s) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) st.w[r] = packed[((size_t)tiles[r] * S + s) * kWave + lane];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int gs = 0; gs < GSUB; ++gs) {
-        const int j = (GSUB == 1) ? s / J : s * GSUB + gs;
-        const size_t gbase = ((size_t)tiles[r] * Gp + j) * 16;
-        st.sc[r][gs] = *reinterpret_cast<const uint2*>(scales + gbase + crow);
-        if (ASYM) st.z[r][gs] = zeros[gbase + arow];
-      }
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      const int b = (col0 + c) * 16 + (lane & 15);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = s * kSuperK + m * kBlockK + 8 * kq;
-        st.x[c][m] = (b < B && k < K) ? as_half8(*reinterpret_cast<const uint4*>(x + (size_t)b * K + k)) : zero8;
-      }
-    }
-  };
-
-  auto compute = [&](const Stage<R, NT, GSUB, ASYM>& st) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int gs = 0; gs < GSUB; ++gs) {
-        const half4_t sh = __builtin_bit_cast(half4_t, st.sc[r][gs]);
-        const float4_t sc = {(float)sh[0], (float)sh[1], (float)sh[2], (float)sh[3]};
-        half2_t blo = sym_lo, bhi = sym_hi;
-        if (ASYM) {
-          const _Float16 z = (_Float16)(float)st.z[r][gs];
-          blo = half2_t{(_Float16)-1024.0f - z, (_Float16)-1024.0f - z};
-          bhi = half2_t{(_Float16)-64.0f - z, (_Float16)-64.0f - z};
-        }
-        half8_t a[MPG];
-#pragma unroll
-        for (int mm = 0; mm < MPG; ++mm) a[mm] = dequant8(lane_dword(st.w[r], gs * MPG + mm), blo, bhi);
-#pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          float4_t part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int mm = 0; mm < MPG; ++mm) part = mfma16x16x32(a[mm], st.x[c][gs * MPG + mm], part);
-          acc[r][c] += sc * part;
-        }
-      }
-    }
-  };
-
-  Stage<R, NT, GSUB, ASYM> buf[P];
-#pragma unroll
-  for (int p = 0; p < P - 1; ++p)
-    if (sb0 + p < sb1) load(buf[p], sb0 + p);
-  for (int s = sb0; s < sb1; s += P) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (s + p + P - 1 < sb1) load(buf[(p + P - 1) % P], s + p + P - 1);
-      if (s + p < sb1) compute(buf[p]);
-    }
-  }
-
-  // Output: accumulator element i of lane l in tile (r, c) is row 16*tile + crow + i,
-  // batch column 16*(col0 + c) + l%16.
-  if (W == 1) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (tile0 + r >= T) continue;
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const int b = (col0 + c) * 16 + (lane & 15);
-        if (b >= B) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = (tile0 + r) * 16 + crow + i;
-          if (n < N) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[r][c][i]);
-        }
-      }
-    }
-    return;
-  }
-
-  constexpr int PER_WAVE = R * NT * 256;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave * PER_WAVE + (r * NT + c) * 256 + i * 64 + lane] = acc[r][c][i];
-  __syncthreads();
-  for (int e = threadIdx.x; e < PER_WAVE; e += blockDim.x) {
-    float sum = 0.f;
-    for (int w = 0; w < W; ++w) sum += red[w * PER_WAVE + e];
-    const int rc = e >> 8, i = (e >> 6) & 3, ln = e & 63;
-    const int r = rc / NT, c = rc % NT;
-    const int n = (tile0 + r) * 16 + 4 * (ln >> 4) + i;
-    const int b = (col0 + c) * 16 + (ln & 15);
-    if (tile0 + r < T && n < N && b < B) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
-  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -606,43 +461,209 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
   }
 }
 
-template <int R, int NT, int GSUB, bool ASYM>
-hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
-  constexpr int P = (NT == 1) ? (R == 4 ? 3 : 4) : 2;
+// ---------------------------------------------------------------------------------
+// Skinny GEMM for B > 16 (MFMA-bound from a few dozen rows of x upward).
+//
+// Workgroup = 4 wavefronts; wavefront w owns row tiles 4*RT*blockIdx.x + RT*w + r,
+// the workgroup owns column tiles CT*blockIdx.y .. + CT - 1 (16 batch rows each).
+// Codes are dequantized exactly to float16 integers (q, or q - z) in registers, as
+// in the GEMV; each group's MFMA partial sum is scaled in float32 and added to the
+// accumulator tile. The activation tile of each 128-channel step (CT*16 rows x 128
+// channels) is staged in double-buffered, padded LDS and read by the four
+// wavefronts as B operands, each read feeding RT row tiles. Codes/scales are
+// prefetched PW steps ahead; the next step's activation tile is loaded into
+// registers before the current step's MFMAs and written to the other LDS buffer
+// after them.
+constexpr int kXRow = kSuperK + 8;  // halfs per LDS row of the activation tile (16-byte pad)
+
+template <int RT, int GSUB, bool ASYM>
+struct GStage {
+  uint4 w[RT];
+  uint2 sc[RT][GSUB];    // float16 scales of the lane's accumulator rows (C layout) per group
+  uint32_t z[RT][GSUB];  // zero point of the lane's A-operand row per group (asymmetric)
+};
+
+template <int RT, int CT, int GSUB, bool ASYM, int PW>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restrict__ x, int B,
+                                                        const uint4* __restrict__ packed,
+                                                        const uint16_t* __restrict__ scales,
+                                                        const uint8_t* __restrict__ zeros, int N, int K, int T,
+                                                        int S, int Gp, int J, uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int MPG = 4 / GSUB;
+  constexpr int XROWS = CT * 16;
+  constexpr int XCH = XROWS * 16 / 256;  // 16-byte chunks of one activation tile per thread
+  uint16_t* xbuf = reinterpret_cast<uint16_t*>(smem);  // [2][XROWS][kXRow]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, arow = lane & 15, crow = 4 * (lane >> 4);
+  const int tile0 = blockIdx.x * 4 * RT + wave * RT;
+  const int b0 = blockIdx.y * XROWS;
+
+  int tiles[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) tiles[r] = min(tile0 + r, T - 1);
+
+  auto load_w = [&](GStage<RT, GSUB, ASYM>& st, int s) {
+    s = min(s, S - 1);  // trailing prefetches re-read the last block: no branch around loads
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const uint4* wp = packed + ((size_t)tiles[r] * S + s) * kWave + lane;
+      st.w[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp)));
+#pragma unroll
+      for (int gs = 0; gs < GSUB; ++gs) {
+        const int j = (GSUB == 1) ? s / J : s * GSUB + gs;
+        const size_t g0 = ((size_t)tiles[r] * Gp + j) * 16;
+        st.sc[r][gs] = *reinterpret_cast<const uint2*>(scales + g0 + crow);
+        if (ASYM) st.z[r][gs] = zeros[g0 + arow];
+      }
+    }
+  };
+  // this thread's chunks of an activation tile: chunk c = threadIdx.x + 256 * i -> row c / 16, 8 halfs at 8 * (c % 16)
+  auto load_x = [&](uint4 (&v)[XCH], int s) {
+    s = min(s, S - 1);
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int b = min(b0 + (c >> 4), B - 1);
+      const int k = min(s * kSuperK + 8 * (c & 15), K - 8);
+      v[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
+    }
+  };
+  auto store_x = [&](const uint4 (&v)[XCH], int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int row = c >> 4, col = 8 * (c & 15);
+      const bool valid = (b0 + row < B) && (s * kSuperK + col < K);
+      *reinterpret_cast<uint4*>(xbuf + (buf * XROWS + row) * kXRow + col) = valid ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  float4_t acc[RT][CT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[r][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 xv[XCH];
+  load_x(xv, 0);
+  GStage<RT, GSUB, ASYM> ring[PW];
+#pragma unroll
+  for (int p = 0; p < PW; ++p) load_w(ring[p], p);
+  store_x(xv, 0, 0);
+  lds_barrier();
+
+  const DequantRegs dq = DequantRegs::make();
+
+  auto step = [&](GStage<RT, GSUB, ASYM>& st, int s) {
+    const int buf = s & 1;
+    load_x(xv, s + 1);  // next activation tile: issued before the next codes (in-order completion)
+    // this block's codes as float16 integers in MFMA A-operand order, and the scales
+    half8_t a[RT][4];
+    float4_t sc[RT][GSUB];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+      for (int gs = 0; gs < GSUB; ++gs) {
+        const _Float16 z = ASYM ? (_Float16)(float)st.z[r][gs] : (_Float16)8.0f;
+        const half2_t blo = {(_Float16)-1024.0f - z, (_Float16)-1024.0f - z};
+        const half2_t bhi = {(_Float16)-64.0f - z, (_Float16)-64.0f - z};
+#pragma unroll
+        for (int mm = 0; mm < MPG; ++mm)
+          a[r][gs * MPG + mm] = dequant8r(lane_dword(st.w[r], gs * MPG + mm), dq, blo, bhi);
+        const half4_t sh = __builtin_bit_cast(half4_t, st.sc[r][gs]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[r][gs][i] = (float)sh[i];
+      }
+    }
+    load_w(st, s + PW);  // codes for PW steps ahead into the slot just consumed
+    const uint16_t* xb = xbuf + (buf * XROWS + (lane & 15)) * kXRow + 8 * kq;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      half8_t bop[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) bop[m] = *reinterpret_cast<const half8_t*>(xb + c * 16 * kXRow + m * kBlockK);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+#pragma unroll
+        for (int gs = 0; gs < GSUB; ++gs) {
+          float4_t part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int mm = 0; mm < MPG; ++mm) part = mfma16x16x32(a[r][gs * MPG + mm], bop[gs * MPG + mm], part);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][c][i] = __builtin_fmaf(sc[r][gs][i], part[i], acc[r][c][i]);
+        }
+      }
+    }
+    store_x(xv, s + 1, buf ^ 1);  // the other buffer was last read in step s-1, before the barrier
+    lds_barrier();
+  };
+
+  for (int s = 0; s < S; s += PW) {
+#pragma unroll
+    for (int p = 0; p < PW; ++p)
+      if (s + p < S) step(ring[p], s + p);
+  }
+
+  // accumulator element i of lane l in tile (r, c): row 16*tile + crow + i, batch row b0 + 16c + l%16
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    if (tile0 + r >= T) continue;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int b = b0 + c * 16 + (lane & 15);
+      if (b >= B) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = (tile0 + r) * 16 + crow + i;
+        if (n < N) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[r][c][i]);
+      }
+    }
+  }
+}
+
+template <int RT, int CT, int GSUB, bool ASYM>
+hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
+  constexpr int PW = 3;
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
-  const int W = a.waves_per_group;
-  const int col_tiles_total = (a.B + 15) / 16;
-  dim3 grid((T + R - 1) / R, (col_tiles_total + NT - 1) / NT);
-  dim3 block(W * kWave);
-  const size_t lds = W > 1 ? (size_t)W * R * NT * 256 * sizeof(float) : 0;
-  hipLaunchKernelGGL((gemm_kernel<R, NT, GSUB, ASYM, P>), grid, block, lds, stream,
+  const int col_tiles = (a.B + 15) / 16;
+  dim3 grid((T + 4 * RT - 1) / (4 * RT), (col_tiles + CT - 1) / CT);
+  const size_t lds = (size_t)2 * CT * 16 * kXRow * 2;
+  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, PW>), grid, dim3(256), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
                      a.Gp, J, static_cast<uint16_t*>(a.y));
   return hipGetLastError();
 }
 
-template <int R, int NT, bool ASYM>
-hipError_t launch_g(const GemmArgs& a, hipStream_t stream) {
-  if (a.group == 32) return launch_t<R, NT, 4, ASYM>(a, stream);
-  if (a.group == 64) return launch_t<R, NT, 2, ASYM>(a, stream);
-  return launch_t<R, NT, 1, ASYM>(a, stream);
+// Only shapes whose accumulators and per-group partial tiles fit the register file
+// (RT * CT * GSUB <= 16) are built; the host never selects the others.
+template <int RT, int CT, int GSUB, bool ASYM>
+hipError_t launch_mfma_fit(const GemmArgs& a, hipStream_t stream) {
+  if constexpr (RT * CT * GSUB <= 16) return launch_mfma_t<RT, CT, GSUB, ASYM>(a, stream);
+  return hipErrorInvalidConfiguration;
 }
 
-template <int R, int NT>
-hipError_t launch_a(const GemmArgs& a, hipStream_t stream) {
-  return a.asym ? launch_g<R, NT, true>(a, stream) : launch_g<R, NT, false>(a, stream);
+template <int RT, int CT, bool ASYM>
+hipError_t launch_mfma_g(const GemmArgs& a, hipStream_t stream) {
+  if (a.group == 32) return launch_mfma_fit<RT, CT, 4, ASYM>(a, stream);
+  if (a.group == 64) return launch_mfma_fit<RT, CT, 2, ASYM>(a, stream);
+  return launch_mfma_fit<RT, CT, 1, ASYM>(a, stream);
 }
 
-template <int NT>
-hipError_t launch_r(const GemmArgs& a, hipStream_t stream) {
-  switch (a.rows_per_wave) {
-    case 1: return launch_a<1, NT>(a, stream);
-    case 2: return launch_a<2, NT>(a, stream);
-    default: return launch_a<4, NT>(a, stream);
-  }
+template <int RT, int CT>
+hipError_t launch_mfma_a(const GemmArgs& a, hipStream_t stream) {
+  return a.asym ? launch_mfma_g<RT, CT, true>(a, stream) : launch_mfma_g<RT, CT, false>(a, stream);
+}
+
+template <int CT>
+hipError_t launch_mfma_r(const GemmArgs& a, hipStream_t stream) {
+  if (a.rows_per_wave == 1) return launch_mfma_a<1, CT>(a, stream);
+  if (a.rows_per_wave == 2) return launch_mfma_a<2, CT>(a, stream);
+  return launch_mfma_a<4, CT>(a, stream);
 }
 
 }  // namespace
@@ -650,9 +671,9 @@ hipError_t launch_r(const GemmArgs& a, hipStream_t stream) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.B <= 16) return launch_gemv(a, stream);
   switch (a.col_tiles) {
-    case 1: return launch_r<1>(a, stream);
-    case 2: return launch_r<2>(a, stream);
-    default: return launch_r<4>(a, stream);
+    case 2: return launch_mfma_r<2>(a, stream);
+    case 4: return launch_mfma_r<4>(a, stream);
+    default: return launch_mfma_r<8>(a, stream);
   }
 }
 

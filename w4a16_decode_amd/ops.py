@@ -174,16 +174,21 @@ def gemm(x, qw: QuantizedWeight, out=None, workspace=None):
 
 
 def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int, k_splits: int = 1,
-                out=None, workspace=None):
-    """q4_gemm_config: q4_gemm with an explicit launch shape (tuning)."""
+                col_tiles: int | None = None, out=None, workspace=None):
+    """q4_gemm_config: q4_gemm with an explicit launch shape (tuning).
+
+    col_tiles defaults to 1 for B <= 16 (GEMV) and to the tiles of 16 rows B needs
+    (2, 4 or 8) for the skinny GEMM."""
     B, out = _prep_gemm(x, qw, out)
     lib = _lib.load()
+    if col_tiles is None:
+        col_tiles = 1 if B <= 16 else min(8, max(2, 1 << ((B + 15) // 16 - 1).bit_length()))
     need = 4 * k_splits * B * qw.out_features if (k_splits > 1 and B <= 16) else 0
     ws_ptr, ws_bytes = _workspace(x, need, workspace)
     st = lib.q4_gemm_config(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(),
                             qw.zeros.data_ptr() if qw.zeros is not None else None, int(qw.asym),
                             qw.out_features, qw.in_features, qw.group, out.data_ptr(), rows_per_wave,
-                            waves_per_group, k_splits, ws_ptr, ws_bytes, _stream(x))
+                            waves_per_group, k_splits, col_tiles, ws_ptr, ws_bytes, _stream(x))
     _check(st)
     return out
 
