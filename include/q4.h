@@ -143,9 +143,10 @@ q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void*
  * semantics (zeros used). Returns Q4_ERR_UNSUPPORTED for shapes the kernels
  * cannot run.
  * B <= 16 (GEMV): `rows_per_wave` row tiles of 16 per wavefront (1, 2 or 4),
- *   `waves_per_group` wavefronts per workgroup (1..8) splitting the channel range,
- *   `k_splits` workgroups splitting it further, `col_tiles` must be 1. The
- *   activation slice of one split must fit the device's LDS per workgroup. Needs
+ *   `waves_per_group` wavefronts per workgroup (1..16; at most 8 are used with
+ *   group < 128 or rows_per_wave 4) sharing its work, `k_splits` workgroups
+ *   splitting the channel range, `col_tiles` must be 1. The activation slice of
+ *   one split must fit the device's LDS per workgroup. Needs
  *   k_splits * B * out * 4 bytes of workspace when k_splits > 1.
  * B > 16 (skinny GEMM): `rows_per_wave` 1, 2 or 4, `waves_per_group` 4,
  *   `k_splits` 1, `col_tiles` 2, 4 or 8 tiles of 16 batch rows per workgroup,

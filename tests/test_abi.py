@@ -94,7 +94,7 @@ def test_gemm_validation(lib):
     assert lib.q4_gemm_asym(FAKE, 1, FAKE, FAKE, None, 16, 128, 128, FAKE, None, 0, None) == 1
     c = lib.q4_gemm_config
     assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 3, 1, 1, 1, None, 0, None) == 5
-    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 9, 1, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 17, 1, 1, None, 0, None) == 5
     assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 0, 0, 0, 1, None, 0, None) == 5
     assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 8, 3, 1, None, 0, None) == 5   # k_splits > blocks
     assert c(FAKE, 16, FAKE, FAKE, None, 0, 16, 8192, 128, FAKE, 1, 8, 1, 1, None, 0, None) == 5  # x slice > LDS

@@ -146,21 +146,22 @@ def test_gemm_launch_shapes_agree(q4):
     xg = to_gpu(x)
     ran = 0
     for R in (1, 2, 4):
-        for Wv in (1, 2, 4, 8):
+        for Wv in (1, 2, 4, 8, 16):
             for KS in (1, 3, 16):
                 say(f"  config R={R} W={Wv} KS={KS}")
                 try:
                     y1 = to_np(q4.gemm_config(xg, qw, R, Wv, KS))
                 except q4.Q4Error as e:
-                    # shapes the kernel cannot run: more wavefronts than 128-channel blocks
-                    # per split, or an activation slice larger than one workgroup stages
-                    assert e.status == 5 and (Wv > (K // 128) // KS or (Wv == 1 and KS == 1)), str(e)
+                    # shapes the kernel cannot run: an activation slice larger than one
+                    # workgroup copies (8 chunks of 16 bytes per thread)
+                    nsb = -(-(K // 128) // KS)
+                    assert e.status == 5 and B * nsb * 16 > 8 * Wv * 64, str(e)
                     continue
                 y2 = to_np(q4.gemm_config(xg, qw, R, Wv, KS))
                 assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "non-deterministic"
                 assert_close(y1, ref, f"R={R} W={Wv} KS={KS}")
                 ran += 1
-    assert ran >= 20
+    assert ran >= 40
 
 
 @pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])

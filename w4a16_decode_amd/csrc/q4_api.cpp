@@ -67,8 +67,9 @@ q4_status hip_status(hipError_t e, const char* what) {
 
 // Launch shape for y = x W^T with B rows (the kernels are described at the top of
 // q4_gemm.hip). B <= 16 runs the persistent GEMV kernel: every workgroup keeps its
-// slice of x (B rows x its channel range) in LDS next to two reduction buffers, so
-// the channel range is split over KS workgroups until that fits the device's LDS.
+// slice of x (B rows x its channel range) in LDS next to its wavefronts' partial
+// sums, so the channel range is split over KS workgroups until that fits the
+// device's LDS.
 constexpr int kGemvXChunks = 8;          // x chunks of 16 B per thread (kXChunksPerThread)
 constexpr size_t kLdsFallback = 64 * 1024;
 
@@ -89,22 +90,25 @@ size_t lds_per_block() {
   return lim;
 }
 
-// LDS of one GEMV workgroup holding one row block (q4_gemm.hip, GemvLds): x slice
-// + zero row, the per-unit biases of symmetric codes, two reduction buffers and
-// the results of one row block. The launch keeps further row blocks' results in
-// what is left of the limit.
-size_t gemv_lds(int B, int S, int KS, int W, int R, int group, bool asym) {
+// LDS of one GEMV workgroup with a single unit of work (q4_gemm.hip, GemvLds): x
+// slice + zero row, the per-unit biases of symmetric codes, the partial sums of
+// one unit and the unit counter. The launch fits as many units as the limit holds.
+size_t gemv_lds(int B, int S, int KS, int R, int group, bool asym) {
   const size_t nsb = (size_t)((S + KS - 1) / KS);
   const size_t gsub = group >= 128 ? 1 : (size_t)(128 / group);
   const size_t x = (((size_t)B * (nsb * 128 + 8) + 128) * 2 + 15) & ~(size_t)15;
   const size_t beta = asym ? 0 : ((size_t)B * nsb * gsub + 1 + 3) / 4 * 4 * sizeof(float);
-  return x + beta + 2 * (size_t)W * R * 1024 + (size_t)R * 16 * B * 4;
+  return x + beta + (size_t)R * 16 * B * 4 + 16;
 }
 
+// Wavefronts a GEMV workgroup runs with (gemv_max_waves in q4_gemm.hip).
+int gemv_max_waves(int R, int group) { return (group < 128 || R > 2) ? 8 : 16; }
+
 bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, size_t lds_limit) {
-  if (KS < 1 || KS > S || W < 1 || W > 8 || W > S / KS) return false;
+  if (KS < 1 || KS > S || W < 1 || W > 16) return false;
+  W = std::min(W, gemv_max_waves(R, group));
   const int nsb = (S + KS - 1) / KS;
-  if (gemv_lds(B, S, KS, W, R, group, asym) > lds_limit) return false;
+  if (gemv_lds(B, S, KS, R, group, asym) > lds_limit) return false;
   return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
 }
 
@@ -127,21 +131,18 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
   const int S = d.Kp / 128;
   const int col_tiles_total = (B + 15) / 16;
   if (B <= 16) {
-    // at most half of a 160 KiB CU, so two 8-wavefront workgroups stay resident
-    const size_t lim = std::min<size_t>(lds_per_block(), 80 * 1024);
+    // a workgroup may use the CU's whole LDS (the activation slice decides how many
+    // stay resident per CU)
+    const size_t lim = lds_per_block();
     a->col_tiles = 1;
-    // one row tile per wavefront for tall matrices and small groups (several scales
-    // per block), two when there are fewer than 2048 tiles (fewer, longer-lived
-    // workgroups amortise the start-up better)
-    int R = (T >= 2048 || d.group < 128) ? 1 : 2;
-    int W = std::min(8, S);
+    // one row tile per wavefront, two for square-ish matrices with few tiles (the
+    // extra tile per load keeps more bytes in flight where there are few row blocks)
+    const int R = (T >= 2048 || d.group < 128 || T > S * 8) ? 1 : 2;
+    // 8 wavefronts (two workgroups per CU) stream best for B <= 4; 16 hold twice
+    // the activation slice, which keeps larger batches from splitting the channels
+    const int W = B <= 4 ? 8 : gemv_max_waves(R, d.group);
     int KS = 1;
-    while (!gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim)) {
-      if (R > 1) { R = 1; continue; }
-      if (KS < S && W <= S / (KS + 1)) { ++KS; continue; }
-      if (W > 1) { W /= 2; KS = 1; continue; }
-      break;  // unreachable for B <= 16: KS = S, W = 1 always fits
-    }
+    while (KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim)) ++KS;
     a->rows_per_wave = R;
     a->waves_per_group = W;
     a->k_splits = KS;
@@ -267,14 +268,14 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
   if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0 || col_tiles > 0) {
     if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
       return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave must be 1, 2 or 4");
-    if (waves_per_group < 1 || waves_per_group > 8)
-      return fail(Q4_ERR_UNSUPPORTED, "waves_per_group must be in [1, 8]");
+    if (waves_per_group < 1 || waves_per_group > 16)
+      return fail(Q4_ERR_UNSUPPORTED, "waves_per_group must be in [1, 16]");
     if (B <= 16) {
       if (col_tiles != 1) return fail(Q4_ERR_UNSUPPORTED, "col_tiles must be 1 for B <= 16");
       a.lds_limit = lds_per_block();
       if (!gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, asym, a.lds_limit))
-        return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: the activation slice of B=%lld and "
-                    "the reduction buffers exceed LDS, or fewer than one 128-channel block per wavefront",
+        return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: more splits than 128-channel blocks, "
+                    "or the activation slice of B=%lld does not fit LDS or the copy",
                     (int)k_splits, (int)waves_per_group, (long long)B);
     } else if (!mfma_shape_ok(rows_per_wave, waves_per_group, k_splits, col_tiles, d.group)) {
       return fail(Q4_ERR_UNSUPPORTED, "for B > 16: waves_per_group must be 4, k_splits 1, col_tiles 2, 4 or 8 "

@@ -42,67 +42,68 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 // ---------------------------------------------------------------------------------
 // GEMV kernel for B <= 16 (one 16-column MFMA tile), persistent.
 //
-// The grid is sized to what the GPU holds at once. Workgroup g owns k-split
-// ks = g % KS of the channel range and the row blocks (R tiles of 16 rows)
-// g/KS, g/KS + G/KS, ... Its W wavefronts split the k-split's channel range; each
-// wavefront streams its blocks of codes and scales for one row block after the
-// other with P-1 blocks in flight (vector loads retire in order, so only weights
-// ride that pipeline), and reads its activation operands from LDS: the workgroup
-// copies its slice of x (all B rows) into LDS once, for all its row blocks. After
-// the last block of a row block the wavefronts' partial sums are reduced through
-// LDS (double-buffered, one barrier per row block) while the loads for the next
-// row block are already in flight. With KS > 1 the workgroups write float32
-// partials to the workspace and reduce_splits_kernel adds them in a fixed order.
+// The grid is sized to what the GPU holds at once (normally one workgroup of 16
+// wavefronts per CU). Workgroup g owns k-split ks = g % KS of the channel range and
+// the row blocks (R tiles of 16 rows) g/KS, g/KS + G/KS, ... Its work is cut into
+// units: one row block times one of CH chunks of the k-split's 128-channel blocks.
+// Wavefronts take units from a counter in LDS as they go, so a wavefront that the
+// SIMD serves faster simply takes more units and all of them finish together (the
+// sequencer favours older wavefronts; a static split leaves the youngest ones
+// streaming alone at the end). Each wavefront streams the blocks of codes and
+// scales of its units with P-1 blocks in flight (vector loads retire in order, so
+// only weights ride that pipeline) and reads its activation operands from LDS: the
+// workgroup copies its slice of x (all B rows) into LDS once. The x loads are all
+// issued before any weight load, so they are not queued behind the first burst
+// of weights. A finished unit's partial sums (the B real columns only) are parked
+// in LDS under the unit's index; after one barrier at the end they are added over
+// the chunks in chunk order, so the result does not depend on which wavefront ran
+// which unit. With KS > 1 the workgroups write float32 partials to the workspace
+// and reduce_splits_kernel adds them in a fixed order.
 template <int R, int GSUB, bool ASYM>
 struct WStage {
   uint4 w[R];
   uint2 sc[R][GSUB];
   uint32_t z[R][GSUB];
+  int s;     // block index (uniform)
+  int unit;  // unit index, or -1 once the wavefront has no more work (uniform)
+  bool last; // last block of its unit (uniform)
 };
 
-constexpr int kXChunksPerThread = 8;  // x slice <= 8 * 16 B * blockDim
+constexpr int kXChunksPerThread = 8;  // x slice <= 8 * 16 B * blockDim (XCH is 2, 4 or 8)
 
 // LDS layout of one GEMV workgroup, in bytes (shared with the host-side sizing).
 struct GemvLds {
-  size_t x, beta, red, out, total;
-  __host__ __device__ GemvLds(int B, int nsb, int GSUB, bool bias, int W, int R, int n_rb) {
+  size_t x, beta, part, total;
+  __host__ __device__ GemvLds(int B, int nsb, int GSUB, bool bias, int R, int units) {
     x = ((((size_t)B * (nsb * kSuperK + 8) + kSuperK) * 2) + 15) & ~(size_t)15;  // x rows + zero row
     beta = bias ? (((size_t)B * nsb * GSUB + 1 + 3) / 4 * 4) * 4 : 0;            // per-unit biases + a zero
-    red = 2 * (size_t)W * R * 256 * 4;                                           // two reduction buffers
-    out = (size_t)n_rb * R * 16 * B * 4;                                         // results until the final store
-    total = x + beta + red + out;
+    part = (size_t)units * R * 16 * B * 4;  // partial sums of every unit
+    total = x + beta + part + 16;           // + the unit counter
   }
 };
 
-#ifndef Q4_GEMV_WAVES_R1
-#define Q4_GEMV_WAVES_R1 4
-#endif
-#ifndef Q4_GEMV_WAVES_R2
-#define Q4_GEMV_WAVES_R2 4
-#endif
-// Register budget for one group per block (g >= 128): at least Q4_GEMV_WAVES_R*
-// wavefronts per SIMD (512 / waves VGPRs). Smaller groups keep more scales per
-// block and run without a budget rather than spill.
-template <int R, int GSUB, bool ASYM, int P, bool NTL>
-__global__ __launch_bounds__(512)
-__attribute__((amdgpu_waves_per_eu((GSUB > 1 || R > 2) ? 1 : (R == 1 ? Q4_GEMV_WAVES_R1 : Q4_GEMV_WAVES_R2), 8)))
-void gemv_kernel(const uint16_t* __restrict__ x, int B,
-                                                   const uint4* __restrict__ packed,
-                                                   const uint16_t* __restrict__ scales,
-                                                   const uint8_t* __restrict__ zeros, int N, int K, int T, int S,
-                                                   int Gp, int J, int KS, int nRB, uint16_t* __restrict__ y,
-                                                   float* __restrict__ ws) {
+// Wavefronts per workgroup the kernel is built for: 16 (one workgroup per CU,
+// 128 VGPRs) for one group per block and R <= 2, else 8 (256 VGPRs) so that the
+// extra scales and row tiles stay in registers.
+template <int R, int GSUB>
+constexpr int gemv_max_waves() { return (GSUB > 1 || R > 2) ? 8 : 16; }
+
+template <int R, int GSUB, bool ASYM, int P, int XCH>
+__global__ __launch_bounds__((gemv_max_waves<R, GSUB>() * 64))
+void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
+                 const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int T,
+                 int S, int Gp, int J, int KS, int nRB, int CH, uint16_t* __restrict__ y,
+                 float* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MPG = 4 / GSUB;
-  constexpr int PER_WAVE = R * 256;  // floats of one wavefront's partial sums
   // Symmetric codes skip the per-pair bias removal (magic8r) and subtract a
-  // per-unit bias from the float32 partial instead; a unit is the channel run one
-  // partial covers (128 / GSUB).
+  // per-unit bias from the float32 partial instead; a bias unit is the channel run
+  // one partial covers (128 / GSUB).
   constexpr bool BIAS = !ASYM;
   constexpr int UNIT = kSuperK / GSUB;
   const int W = blockDim.x >> 6;
   // readfirstlane: the wavefront index is uniform, and saying so keeps every value
-  // derived from it (block ranges, addresses, loop bounds) in scalar registers
+  // derived from it in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ks = blockIdx.x % KS;
@@ -110,66 +111,85 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B,
   const int rb_stride = gridDim.x / KS;
   const int wsb0 = (int)(((int64_t)S * ks) / KS);
   const int wsb1 = (int)(((int64_t)S * (ks + 1)) / KS);
-  const int nsb = wsb1 - wsb0;
-  const int sb0 = wsb0 + (int)(((int64_t)nsb * wave) / W);
-  const int sb1 = wsb0 + (int)(((int64_t)nsb * (wave + 1)) / W);
-  const int nsw = sb1 - sb0;  // >= 1: the host keeps W <= S / KS
+  const int nsb = wsb1 - wsb0;  // >= CH: the host keeps every chunk at least one block long
   const int n_rb = rb_first < nRB ? (nRB - 1 - rb_first) / rb_stride + 1 : 0;
-  const int total = n_rb * nsw;  // blocks this wavefront streams
+  const int n_units = n_rb * CH;
   const int KR = nsb * kSuperK;
   const int xstride = KR + 8;  // halfs per x row in LDS (16-byte pad against bank conflicts)
   const int nunits = nsb * GSUB;
-  const GemvLds lay(B, nsb, GSUB, BIAS, W, R, n_rb);
+  const GemvLds lay(B, nsb, GSUB, BIAS, R, n_units);
   uint16_t* xl = reinterpret_cast<uint16_t*>(smem);      // x (x/16 at the scaled elements when BIAS)
   uint16_t* xzero = xl + B * xstride;                     // 128 zero halfs for absent batch rows
   float* beta = reinterpret_cast<float*>(smem + lay.x);
-  float* red0 = reinterpret_cast<float*>(smem + lay.x + lay.beta);
-  float* outb = reinterpret_cast<float*>(smem + lay.x + lay.beta + lay.red);
-  const int kq = lane >> 4;
+  float* part0 = reinterpret_cast<float*>(smem + lay.x + lay.beta);  // [unit][r][b][16 rows]
+  int* counter = reinterpret_cast<int*>(smem + lay.x + lay.beta + lay.part);
   const int crow = 4 * (lane >> 4);
   const int arow = lane & 15;
   const int bcol = lane & 15;
 
-  // 1. the workgroup's x slice -> registers. Every load is issued (indices clamped
-  //    into x) so the wait before the LDS copy counts exactly these loads, not the
-  //    weight loads issued after them.
+  // 1. the workgroup's x slice -> registers: XCH chunks of 16 bytes per thread, the
+  //    fewest that cover it (indices clamped into x, so every thread issues the same
+  //    number of loads and the later wait is exact)
   const int row_chunks = KR >> 3;
   const int xchunks = B * row_chunks;
-  uint4 xr[kXChunksPerThread];
+  uint4 xr[XCH];
 #pragma unroll
-  for (int i = 0; i < kXChunksPerThread; ++i) {
+  for (int i = 0; i < XCH; ++i) {
     const int idx = min((int)threadIdx.x + i * (int)blockDim.x, xchunks - 1);
     const int b = idx / row_chunks;
     const int k = min(wsb0 * kSuperK + (idx - b * row_chunks) * 8, K - 8);
     xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
   }
+  if (threadIdx.x == 0) *counter = 0;
+  lds_barrier();  // every x load is issued before any weight load; the counter is set
 
   // 2. the first P-1 blocks of codes / scales. Block addresses are wave-uniform
   //    (tile base + 1 KiB per block); only the lane offsets live in VGPRs. Loads are
-  //    unconditional: after the last block the counters stay put and the trailing
-  //    prefetches re-read it, which keeps the loop free of branches around loads.
+  //    unconditional: once the units run out the last block is loaded again, which
+  //    keeps the loop free of branches around loads.
   const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
   const uint32_t w_lane = (uint32_t)lane * 16u;
   const uint32_t s_lane = (uint32_t)crow * 2u;
-  int l_rb = rb_first, l_s = sb0, loads_left = total;
-  int l_j = (GSUB == 1) ? sb0 / J : sb0 * GSUB, l_jr = (GSUB == 1) ? sb0 % J : 0;
+  int l_unit = 0, l_s = 0, l_send = 0, l_j = 0, l_jr = 0;
   const unsigned char* l_wt[R];
   const unsigned char* l_st[R];
-  auto set_tiles = [&]() {
+  auto grab = [&]() __attribute__((always_inline)) {
+    // every lane adds 1 (called with all lanes active), so a grab moves the counter
+    // by 64 and each lane sees a value in [64u, 64u + 63]
+    const int u = __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;
+    if (u >= n_units) {
+      l_unit = -1;  // the address registers keep the last unit (loads clamp the block)
+      return;
+    }
+    l_unit = u;
+    const int i = u / CH, c = u - i * CH;
+    l_s = wsb0 + nsb * c / CH;  // nsb * CH < 2^31: CH <= 64
+    l_send = wsb0 + nsb * (c + 1) / CH;
+    l_j = (GSUB == 1) ? l_s / J : l_s * GSUB;
+    l_jr = (GSUB == 1) ? l_s - (l_s / J) * J : 0;
+    const int rb = rb_first + i * rb_stride;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const size_t tile = (size_t)min(l_rb * R + r, T - 1);
+      const size_t tile = (size_t)min(rb * R + r, T - 1);
       l_wt[r] = pk + tile * S * 1024;
       l_st[r] = reinterpret_cast<const unsigned char*>(scales) + tile * Gp * 32;
     }
   };
-  set_tiles();
-  auto load = [&](WStage<R, GSUB, ASYM>& st) {
+  grab();
+  if (l_unit < 0) {  // no work for this wavefront: point the (unused) loads at tile 0
+    l_s = wsb0;
+    l_j = (GSUB == 1) ? wsb0 / J : wsb0 * GSUB;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const unsigned char* wp = l_wt[r] + (size_t)l_s * 1024 + w_lane;
-      if (NTL) st.w[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp)));
-      else st.w[r] = *reinterpret_cast<const uint4*>(wp);
+      l_wt[r] = pk;
+      l_st[r] = reinterpret_cast<const unsigned char*>(scales);
+    }
+  }
+  auto load = [&](WStage<R, GSUB, ASYM>& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const unsigned char* wp = l_wt[r] + (size_t)min(l_s, S - 1) * 1024 + w_lane;
+      st.w[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp)));
 #pragma unroll
       for (int gs = 0; gs < GSUB; ++gs) {
         const size_t goff = (size_t)(l_j + gs) * 32;
@@ -178,7 +198,14 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B,
                                       (goff >> 1) + arow];
       }
     }
-    if (--loads_left <= 0) return;
+    st.s = min(l_s, wsb1 - 1);
+    st.unit = l_unit;
+    st.last = l_s + 1 == l_send;
+    if (l_unit < 0) return;
+    if (++l_s == l_send) {
+      grab();
+      return;
+    }
     if (GSUB == 1) {
       if (++l_jr == J) {
         l_jr = 0;
@@ -187,98 +214,83 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B,
     } else {
       l_j += GSUB;
     }
-    if (++l_s == sb1) {
-      l_s = sb0;
-      l_j = (GSUB == 1) ? sb0 / J : sb0 * GSUB;
-      l_jr = (GSUB == 1) ? sb0 % J : 0;
-      l_rb += rb_stride;
-      set_tiles();
-    }
   };
   WStage<R, GSUB, ASYM> buf[P];
 #pragma unroll
   for (int p = 0; p < P - 1; ++p) load(buf[p]);
 
   // 3. x slice -> LDS (elements 2, 3, 6, 7 of every 8 divided by 16 when BIAS: exact
-  //    powers of two; channels past K are zero), plus the zero row
+  //    powers of two; channels past K are zero), plus the zero row. With BIAS the
+  //    per-unit bias 1032 * (sum of plain elements) + 1152 * (sum of scaled elements)
+  //    is reduced on the way: the UNIT / 8 chunks of a bias unit sit in consecutive
+  //    lanes (row_chunks is a multiple of 16 and the block a multiple of 64 threads).
+  constexpr int CPU = UNIT / 8;  // chunks per bias unit
 #pragma unroll
-  for (int i = 0; i < kXChunksPerThread; ++i) {
+  for (int i = 0; i < XCH; ++i) {
     const int idx = threadIdx.x + i * blockDim.x;
-    if (idx < xchunks) {
-      const int b = idx / row_chunks;
-      const int c8 = idx - b * row_chunks;
-      uint4 v = (wsb0 * kSuperK + c8 * 8 < K) ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
-      if (BIAS) {
-        half8_t h = as_half8(v);
-        h[2] *= (_Float16)0.0625f;
-        h[3] *= (_Float16)0.0625f;
-        h[6] *= (_Float16)0.0625f;
-        h[7] *= (_Float16)0.0625f;
-        v = __builtin_bit_cast(uint4, h);
+    if (i * (int)blockDim.x >= xchunks) break;  // uniform: no chunk of this round is real
+    const bool real = idx < xchunks;
+    const int b = idx / row_chunks;
+    const int c8 = idx - b * row_chunks;
+    uint4 v = (real && wsb0 * kSuperK + c8 * 8 < K) ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
+    if (BIAS) {
+      half8_t h = as_half8(v);
+      h[2] *= (_Float16)0.0625f;
+      h[3] *= (_Float16)0.0625f;
+      h[6] *= (_Float16)0.0625f;
+      h[7] *= (_Float16)0.0625f;
+      v = __builtin_bit_cast(uint4, h);
+      float plain = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
+      float scaled = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
+#pragma unroll
+      for (int m = 1; m < CPU; m <<= 1) {
+        plain += __shfl_xor(plain, m);
+        scaled += __shfl_xor(scaled, m);
       }
-      *reinterpret_cast<uint4*>(xl + b * xstride + c8 * 8) = v;
+      if (real && c8 % CPU == 0) beta[b * nunits + c8 / CPU] = 1032.f * plain + 1152.f * scaled;
     }
+    if (real) *reinterpret_cast<uint4*>(xl + b * xstride + c8 * 8) = v;
   }
   if (threadIdx.x < kSuperK / 8) *reinterpret_cast<uint4*>(xzero + threadIdx.x * 8) = make_uint4(0u, 0u, 0u, 0u);
+  if (BIAS && threadIdx.x == 0) beta[B * nunits] = 0.f;
   lds_barrier();
-  if (BIAS) {
-    // bias of every (batch row, unit): 1032 * (sum of plain elements) + 1152 * (sum of scaled elements)
-    for (int e = threadIdx.x; e < B * nunits; e += blockDim.x) {
-      const int b = e / nunits, u = e - b * nunits;
-      const uint16_t* xs = xl + b * xstride + u * UNIT;
-      float plain = 0.f, scaled = 0.f;
-      for (int c = 0; c < UNIT; c += 8) {
-        const half8_t h = *reinterpret_cast<const half8_t*>(xs + c);
-        plain += ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
-        scaled += ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
-      }
-      beta[e] = 1032.f * plain + 1152.f * scaled;
-    }
-    if (threadIdx.x == 0) beta[B * nunits] = 0.f;
-    lds_barrier();
-  }
 
   float4_t acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
   const DequantRegs dq = DequantRegs::make();
   // LDS read pointers of this lane's activation operand and bias; lanes of absent
-  // batch rows stay on the zero row / zero bias (step 0)
+  // batch rows stay on the zero row / zero bias
   const bool real_col = bcol < B;
-  const uint16_t* xlane0 = real_col ? xl + bcol * xstride + (sb0 - wsb0) * kSuperK + 8 * kq : xzero + 8 * kq;
+  const uint16_t* xlane0 = real_col ? xl + bcol * xstride + 8 * (lane >> 4) : xzero + 8 * (lane >> 4);
   const int xstep = real_col ? kSuperK : 0;
-  const float* blane0 = real_col ? beta + bcol * nunits + (sb0 - wsb0) * GSUB : beta + B * nunits;
+  const float* blane0 = real_col ? beta + bcol * nunits : beta + B * nunits;
   const int bstep = real_col ? GSUB : 0;
-  const uint16_t* xp = xlane0;
-  const float* bp = blane0;
-  int c_i = 0, c_s = sb0, parity = 0;  // row block (index among this workgroup's) and block being computed
 
-  // activation operands (and biases) of the block being computed, read from LDS
-  // one block ahead so the LDS latency hides behind the previous block's work
+  // activation operands (and biases) of the next block to compute, read from LDS
+  // one block ahead so the LDS latency hides behind the current block's work
   half8_t xb[4];
   float bu[GSUB];
-  auto read_x = [&]() {
+  auto read_x = [&](int s) __attribute__((always_inline)) {
+    const uint16_t* xp = xlane0 + (s - wsb0) * xstep;
 #pragma unroll
     for (int m = 0; m < 4; ++m) xb[m] = *reinterpret_cast<const half8_t*>(xp + m * kBlockK);
     if (BIAS) {
+      const float* bp = blane0 + (s - wsb0) * bstep;
 #pragma unroll
       for (int gs = 0; gs < GSUB; ++gs) bu[gs] = bp[gs];
     }
   };
-  read_x();
+  read_x(buf[0].s);
 
-  auto compute = [&](const WStage<R, GSUB, ASYM>& st) {
+  auto compute = [&](const WStage<R, GSUB, ASYM>& st, int s_next) __attribute__((always_inline)) {
     half8_t xc[4];
     float bc[GSUB];
 #pragma unroll
     for (int m = 0; m < 4; ++m) xc[m] = xb[m];
 #pragma unroll
     for (int gs = 0; gs < GSUB; ++gs) bc[gs] = BIAS ? bu[gs] : 0.f;
-    // next block of the same row block, or the first block of the next one
-    const bool last = c_s + 1 == sb1;
-    xp = last ? xlane0 : xp + xstep;
-    bp = last ? blane0 : bp + bstep;
-    read_x();
+    read_x(s_next);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -303,51 +315,44 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B,
         }
       }
     }
-    if (++c_s < sb1) return;
-    // Row block finished: reduce the W partial sums into the LDS result buffer
-    // (every wavefront gets here once per row block; no global memory access).
-    float* red = red0 + parity * (W * PER_WAVE);
+    if (!st.last) return;
+    // unit finished: park the partial sums of the real batch columns (the lane
+    // holds rows crow..crow+3 of column bcol) and start the next unit from zero
+    if (real_col) {
+      float* pp = part0 + (size_t)st.unit * R * 16 * B + bcol * 16 + crow;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave * PER_WAVE + r * 256 + i * 64 + lane] = acc[r][i];
-    lds_barrier();
-    for (int e = threadIdx.x; e < PER_WAVE; e += blockDim.x) {
-      const int ln = e & 63;
-      const int b = ln & 15;
-      if (b < B) {
-        float sum = 0.f;
-        for (int w = 0; w < W; ++w) sum += red[w * PER_WAVE + e];
-        const int r = e >> 8, i = (e >> 6) & 3;
-        outb[((c_i * R + r) * 16 + 4 * (ln >> 4) + i) * B + b] = sum;
-      }
+      for (int r = 0; r < R; ++r) *reinterpret_cast<float4_t*>(pp + r * 16 * B) = acc[r];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
-    parity ^= 1;
-    c_s = sb0;
-    ++c_i;
   };
 
-  for (int it = 0; it < total; it += P) {
+  // once a stage has no unit, every later one has none either
+  while (buf[0].unit >= 0) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       load(buf[(p + P - 1) % P]);
-      if (it + p < total) compute(buf[p]);
+      if (buf[p].unit >= 0) compute(buf[p], buf[(p + 1) % P].s);
     }
   }
 
-  // 4. results of all row blocks: LDS -> y (or the k-split workspace)
+  // 4. results of all row blocks: the units' partials added in chunk order -> y
+  //    (or the k-split workspace); e = ((i * R + r) * B + b) * 16 + row
   lds_barrier();
   const int nout = n_rb * R * 16 * B;
   for (int e = threadIdx.x; e < nout; e += blockDim.x) {
-    const int b = e % B;
-    const int rowi = e / B;  // (i * R + r) * 16 + row
-    const int i = rowi / (R * 16), rr = rowi % (R * 16);
-    const int n = (rb_first + i * rb_stride) * R * 16 + rr;
+    const int row = e & 15;
+    const int t = e >> 4;
+    const int b = t % B;
+    const int ir = t / B;  // i * R + r
+    const int i = ir / R, r = ir - i * R;
+    const float* pp = part0 + ((size_t)i * CH * R + r) * 16 * B + b * 16 + row;
+    float sum = 0.f;
+    for (int c = 0; c < CH; ++c) sum += pp[(size_t)c * R * 16 * B];
+    const int n = ((rb_first + i * rb_stride) * R + r) * 16 + row;
     if (n < N) {
-      if (KS == 1) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)outb[e]);
-      else ws[((size_t)ks * B + b) * N + n] = outb[e];
+      if (KS == 1) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+      else ws[((size_t)ks * B + b) * N + n] = sum;
     }
   }
 }
@@ -390,47 +395,49 @@ int device_cus() {
   return cus;
 }
 
-template <int R, int GSUB, bool ASYM>
+template <int R, int GSUB, bool ASYM, int XCH>
 hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
-#ifndef Q4_GEMV_DEPTH_R1
-#define Q4_GEMV_DEPTH_R1 8
-#endif
-#ifndef Q4_GEMV_DEPTH_R2
-#define Q4_GEMV_DEPTH_R2 4
-#endif
-  // pipeline depth (blocks of codes in flight + 1) per row-tile count; fixed at
-  // build time (the macros exist so tuning builds can try other depths)
-  constexpr int P = R == 1 ? Q4_GEMV_DEPTH_R1 : (R == 2 ? Q4_GEMV_DEPTH_R2 : 4);
-  constexpr bool NTL = true;
+  // pipeline depth (blocks of codes in flight + 1) per row-tile count
+  constexpr int P = R == 1 ? 8 : 4;
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
-  const int W = a.waves_per_group;
+  const int W = std::min(a.waves_per_group, gemv_max_waves<R, GSUB>());
   const int KS = a.k_splits;
   const int nRB = (T + R - 1) / R;
   const int max_nsb = (S + KS - 1) / KS;
-  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, NTL>);
-  // Persistent grid: as many workgroups as stay resident (measured with the LDS of
-  // one row block per workgroup), with the row blocks spread evenly over them; more
-  // workgroups if the per-workgroup result buffer would not fit.
-  const size_t lds1 = GemvLds(a.B, max_nsb, GSUB, !ASYM, W, R, 1).total;
-  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, lds1) * device_cus();
-  const int64_t units = (int64_t)nRB * KS;
-  int64_t rounds = (units + resident - 1) / resident;
-  // each further row block per workgroup adds its results to the LDS buffer
-  const size_t out1 = (size_t)R * 16 * a.B * 4;
-  const size_t lim = a.lds_limit > lds1 ? a.lds_limit : lds1;
-  const int64_t max_rounds = std::max<int64_t>(1, (int64_t)((lim - lds1) / out1) + 1);
-  rounds = std::min(rounds, max_rounds);
-  int64_t per_split = ((int64_t)nRB + rounds - 1) / rounds;
+  const int min_nsb = S / KS;  // >= 1: the host keeps KS <= S
+  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH>);
+  const size_t lim = a.lds_limit;
+  const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
+  const size_t base = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, 0).total;
+  // Persistent grid: as many workgroups as stay resident, the row blocks spread
+  // evenly over them; more workgroups only if one row block per chunk would not
+  // fit the LDS limit.
+  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, base + unit_bytes) * device_cus();
+  int64_t per_split = std::max<int64_t>(1, std::min<int64_t>(nRB, resident / KS));
   if (a.grid_limit > 0) per_split = std::min<int64_t>(per_split, std::max(1, a.grid_limit / KS));
-  const int n_rb_max = (int)((nRB + per_split - 1) / per_split);
-  const size_t lds = GemvLds(a.B, max_nsb, GSUB, !ASYM, W, R, n_rb_max).total;
+  int n_rb = (int)((nRB + per_split - 1) / per_split);
+  const int64_t max_rb = std::max<int64_t>(1, (int64_t)((lim - std::min(lim, base)) / unit_bytes));
+  if (n_rb > max_rb) {
+    n_rb = (int)max_rb;
+    per_split = (nRB + n_rb - 1) / n_rb;
+  }
+  n_rb = (int)((nRB + per_split - 1) / per_split);
+  // chunks per row block: 8 blocks (8 KiB of codes per tile) each, which streams
+  // best; shorter ones if that leaves fewer than two units per wavefront; at most
+  // 64 and as many as the LDS holds
+  int CH = std::max(1, min_nsb / 8);
+  if ((int64_t)CH * n_rb < 2 * W) CH = (int)std::min<int64_t>(min_nsb, (2 * W + n_rb - 1) / n_rb);
+  CH = std::min(CH, 64);
+  CH = (int)std::min<int64_t>(CH, std::max<int64_t>(1, (int64_t)((lim - std::min(lim, base)) / (unit_bytes * n_rb))));
+  CH = std::max(CH, 1);
+  const size_t lds = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, n_rb * CH).total;
   const int grid = (int)(per_split * KS);
-  hipLaunchKernelGGL((gemv_kernel<R, GSUB, ASYM, P, NTL>), dim3(grid), dim3(W * kWave), lds, stream,
+  hipLaunchKernelGGL((gemv_kernel<R, GSUB, ASYM, P, XCH>), dim3(grid), dim3(W * kWave), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
-                     a.Gp, J, KS, nRB, static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
+                     a.Gp, J, KS, nRB, CH, static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
   if (KS > 1) {
     const int64_t BN = (int64_t)a.B * a.N;
     int64_t blocks = (BN + 255) / 256;
@@ -441,11 +448,23 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// x chunks of 16 bytes each thread copies: the fewest of 2, 4, 8 that cover the
+// activation slice of the largest split
+template <int R, int GSUB, bool ASYM>
+hipError_t launch_gemv_x(const GemmArgs& a, hipStream_t stream) {
+  const int W = std::min(a.waves_per_group, gemv_max_waves<R, GSUB>());
+  const int64_t max_nsb = (a.Kp / kSuperK + a.k_splits - 1) / a.k_splits;
+  const int64_t per_thread = ((int64_t)a.B * max_nsb * 16 + W * kWave - 1) / (W * kWave);
+  if (per_thread <= 2) return launch_gemv_t<R, GSUB, ASYM, 2>(a, stream);
+  if (per_thread <= 4) return launch_gemv_t<R, GSUB, ASYM, 4>(a, stream);
+  return launch_gemv_t<R, GSUB, ASYM, 8>(a, stream);
+}
+
 template <int R, bool ASYM>
 hipError_t launch_gemv_g(const GemmArgs& a, hipStream_t stream) {
-  if (a.group == 32) return launch_gemv_t<R, 4, ASYM>(a, stream);
-  if (a.group == 64) return launch_gemv_t<R, 2, ASYM>(a, stream);
-  return launch_gemv_t<R, 1, ASYM>(a, stream);
+  if (a.group == 32) return launch_gemv_x<R, 4, ASYM>(a, stream);
+  if (a.group == 64) return launch_gemv_x<R, 2, ASYM>(a, stream);
+  return launch_gemv_x<R, 1, ASYM>(a, stream);
 }
 
 template <int R>

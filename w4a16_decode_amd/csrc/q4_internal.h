@@ -43,7 +43,7 @@ struct GemmArgs {
   void* y;
   // launch shape
   int rows_per_wave;    // row tiles of 16 per wavefront: 1, 2 or 4
-  int waves_per_group;  // wavefronts per workgroup splitting the channels: 1..16
+  int waves_per_group;  // wavefronts per workgroup: 1..16 (GEMV), 4 (skinny GEMM)
   int col_tiles;        // 16-column batch tiles per wavefront: 1, 2 or 4
   int k_splits;         // workgroups splitting the channels (B <= 16 path); > 1 needs workspace
   void* workspace;      // float32 [k_splits][B][N] partial sums when k_splits > 1
