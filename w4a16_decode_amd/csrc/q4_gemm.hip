@@ -365,6 +365,289 @@ __global__ void reduce_splits_kernel(const float* __restrict__ ws, int KS, int64
   }
 }
 
+// ---------------------------------------------------------------------------------
+// GEMV for B = 1 with the activation streamed per unit.
+//
+// Same units, counter, partial sums and final reduction as gemv_kernel, but no
+// workgroup-wide copy of x: a unit is always 8 blocks (1024 channels), and the
+// wavefront that takes a unit loads that unit's 1024 activations itself, in
+// the same in-order stream as the unit's codes (2 loads of 16 bytes per lane,
+// issued right before the unit's first codes). When it finishes its
+// previous unit it writes them (and the per-block biases of symmetric codes) into
+// its own slice of LDS, from which the MFMA operands are read as in gemv_kernel.
+// The kernel therefore starts streaming codes at once instead of first staging the
+// whole activation slice, and x is read from L2 in small pieces spread over the
+// kernel. Units are at least P - 1 blocks long, so a wavefront never has the x of
+// more than one unit waiting in registers.
+constexpr int kUnitBlocks = 8;
+constexpr int kUnitXStride = kUnitBlocks * kSuperK + 8;  // halfs per batch row of a unit's x in LDS
+
+// LDS of one streaming workgroup, in bytes (shared with the host-side sizing).
+struct GemvStreamLds {
+  size_t xw, bw, zero, part, total;
+  __host__ __device__ GemvStreamLds(int BMAX, int GSUB, bool bias, int W, int R, int B, int units) {
+    xw = (size_t)W * BMAX * kUnitXStride * 2;                   // per-wavefront x of its unit
+    bw = bias ? (size_t)W * BMAX * kUnitBlocks * GSUB * 4 : 0;  // per-wavefront biases of its unit
+    zero = kSuperK * 2 + 16;                                    // zero row + zero bias
+    part = (size_t)units * R * 16 * B * 4;
+    total = xw + bw + zero + part + 16;  // + the unit counter
+  }
+};
+
+// Stage of the streaming GEMV: codes, scales and one packed word of metadata,
+// unit << 4 | block-in-unit << 1 | last-block-of-unit, or -1 once the wavefront
+// has no more work (uniform, so it lives in one scalar register).
+template <int R, int GSUB, bool ASYM>
+struct SStage {
+  uint4 w[R];
+  uint2 sc[R][GSUB];
+  uint32_t z[R][GSUB];
+  int meta;
+};
+
+// Register budget: 128 VGPRs (two 8-wavefront workgroups per CU) with one group
+// per block; smaller groups keep more scales in flight and run with 256.
+template <int R, int GSUB, bool ASYM, int P>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSUB == 1 ? 4 : 1, 8)))
+void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
+                        const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K,
+                        int T, int S, int Gp, int J, int nRB, uint16_t* __restrict__ y) {
+  static_assert(P - 1 <= kUnitBlocks, "a unit must outlast the blocks in flight");
+  constexpr int BMAX = 1;  // one batch row
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int MPG = 4 / GSUB;
+  constexpr bool BIAS = !ASYM;
+  constexpr int CPU = kSuperK / GSUB / 8;  // 16-byte chunks per bias unit
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int rb_first = blockIdx.x;
+  const int rb_stride = gridDim.x;
+  const int CH = S / kUnitBlocks;  // the host keeps S a multiple of 8
+  const int n_rb = rb_first < nRB ? (nRB - 1 - rb_first) / rb_stride + 1 : 0;
+  const int n_units = n_rb * CH;
+  const GemvStreamLds lay(BMAX, GSUB, BIAS, W, R, B, n_units);
+  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + (size_t)wave * BMAX * kUnitXStride;
+  float* bw = reinterpret_cast<float*>(smem + lay.xw) + (size_t)wave * BMAX * kUnitBlocks * GSUB;
+  uint16_t* xzero = reinterpret_cast<uint16_t*>(smem + lay.xw + lay.bw);
+  float* bzero = reinterpret_cast<float*>(smem + lay.xw + lay.bw + kSuperK * 2);
+  float* part0 = reinterpret_cast<float*>(smem + lay.xw + lay.bw + lay.zero);  // [unit][r][b][16 rows]
+  int* counter = reinterpret_cast<int*>(smem + lay.xw + lay.bw + lay.zero + lay.part);
+  const int crow = 4 * (lane >> 4);
+  const int arow = lane & 15;
+  const int bcol = lane & 15;
+  const int kq = lane >> 4;
+
+  if (threadIdx.x < kSuperK / 8) *reinterpret_cast<uint4*>(xzero + threadIdx.x * 8) = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) {
+    *bzero = 0.f;
+    *counter = 0;
+  }
+  lds_barrier();
+
+  // load side: the unit being streamed, its next block and scale group
+  const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
+  const uint32_t w_lane = (uint32_t)lane * 16u;
+  const uint32_t s_lane = (uint32_t)crow * 2u;
+  int l_unit = -1, l_s = 0, l_s0 = 0, l_j = 0, l_jr = 0;
+  const unsigned char* l_wt[R];
+  const unsigned char* l_st[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    l_wt[r] = pk;
+    l_st[r] = reinterpret_cast<const unsigned char*>(scales);
+  }
+  uint4 xn[BMAX][2];  // x of the unit taken last: channels 8 * (lane + 64 i) of its 1024, per batch row
+  auto grab = [&]() __attribute__((always_inline)) {
+    const int u = __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;  // all lanes add: +64 per grab
+    if (u < n_units) {
+      l_unit = u;
+      const int i = u / CH, c = u - i * CH;
+      l_s0 = l_s = c * kUnitBlocks;
+      l_j = (GSUB == 1) ? l_s / J : l_s * GSUB;
+      l_jr = (GSUB == 1) ? l_s - (l_s / J) * J : 0;
+      const int rb = rb_first + i * rb_stride;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const size_t tile = (size_t)min(rb * R + r, T - 1);
+        l_wt[r] = pk + tile * S * 1024;
+        l_st[r] = reinterpret_cast<const unsigned char*>(scales) + tile * Gp * 32;
+      }
+    } else {
+      l_unit = -1;  // addresses keep the last unit; the loads below repeat its x
+    }
+    // the unit's activations, ahead of its codes (issued on every grab, so the
+    // number of loads in flight does not depend on the outcome)
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k = min(l_s0 * kSuperK + 8 * (lane + 64 * i), K - 8);
+        xn[b][i] = *reinterpret_cast<const uint4*>(x + (size_t)min(b, B - 1) * K + k);
+      }
+  };
+  auto load = [&](SStage<R, GSUB, ASYM>& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const unsigned char* wp = l_wt[r] + (size_t)min(l_s, S - 1) * 1024 + w_lane;
+      st.w[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp)));
+#pragma unroll
+      for (int gs = 0; gs < GSUB; ++gs) {
+        const size_t goff = (size_t)(l_j + gs) * 32;
+        st.sc[r][gs] = *reinterpret_cast<const uint2*>(l_st[r] + goff + s_lane);
+        if (ASYM) st.z[r][gs] = zeros[(size_t)((l_st[r] - reinterpret_cast<const unsigned char*>(scales)) >> 1) +
+                                      (goff >> 1) + arow];
+      }
+    }
+    st.meta = l_unit < 0 ? -1 : (l_unit << 4) | ((l_s - l_s0) << 1) | (l_s + 1 == l_s0 + kUnitBlocks ? 1 : 0);
+    if (l_unit < 0) return;
+    if (++l_s == l_s0 + kUnitBlocks) {
+      grab();
+      return;
+    }
+    if (GSUB == 1) {
+      if (++l_jr == J) {
+        l_jr = 0;
+        ++l_j;
+      }
+    } else {
+      l_j += GSUB;
+    }
+  };
+
+  // the unit's x (x/16 at elements 2, 3, 6, 7 when BIAS; channels past K are zero)
+  // -> this wavefront's LDS, with the per-block biases 1032 * sum(plain) +
+  // 1152 * sum(scaled) reduced over the CPU lanes of each bias unit
+  auto write_x = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+      if (b >= B) break;  // uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c8 = lane + 64 * i;  // 16-byte chunk of the unit's 1024 channels
+        uint4 v = (l_s0 * kSuperK + 8 * c8 < K) ? xn[b][i] : make_uint4(0u, 0u, 0u, 0u);
+        if (BIAS) {
+          half8_t h = as_half8(v);
+          h[2] *= (_Float16)0.0625f;
+          h[3] *= (_Float16)0.0625f;
+          h[6] *= (_Float16)0.0625f;
+          h[7] *= (_Float16)0.0625f;
+          v = __builtin_bit_cast(uint4, h);
+          float plain = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
+          float scaled = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
+#pragma unroll
+          for (int m = 1; m < CPU; m <<= 1) {
+            plain += __shfl_xor(plain, m);
+            scaled += __shfl_xor(scaled, m);
+          }
+          if (c8 % CPU == 0) bw[b * kUnitBlocks * GSUB + c8 / CPU] = 1032.f * plain + 1152.f * scaled;
+        }
+        *reinterpret_cast<uint4*>(xw + b * kUnitXStride + 8 * c8) = v;
+      }
+    }
+  };
+
+  grab();
+  SStage<R, GSUB, ASYM> buf[P];
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p) load(buf[p]);
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const DequantRegs dq = DequantRegs::make();
+  const bool real_col = bcol < B;
+  const uint16_t* xlane0 = real_col ? xw + bcol * kUnitXStride + 8 * kq : xzero + 8 * kq;
+  const int xstep = real_col ? kSuperK : 0;
+  const float* blane0 = real_col ? bw + bcol * kUnitBlocks * GSUB : bzero;
+  const int bstep = real_col ? GSUB : 0;
+  half8_t xb[4];
+  float bu[GSUB];
+  auto read_x = [&](int j) __attribute__((always_inline)) {
+    const uint16_t* xp = xlane0 + j * xstep;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xb[m] = *reinterpret_cast<const half8_t*>(xp + m * kBlockK);
+    if (BIAS) {
+      const float* bp = blane0 + j * bstep;
+#pragma unroll
+      for (int gs = 0; gs < GSUB; ++gs) bu[gs] = bp[gs];
+    }
+  };
+  if (buf[0].meta >= 0) write_x();  // the first unit's x (its loads are the oldest in flight)
+  read_x(0);
+
+  auto compute = [&](const SStage<R, GSUB, ASYM>& st, const SStage<R, GSUB, ASYM>& nx) __attribute__((always_inline)) {
+    half8_t xc[4];
+    float bc[GSUB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xc[m] = xb[m];
+#pragma unroll
+    for (int gs = 0; gs < GSUB; ++gs) bc[gs] = BIAS ? bu[gs] : 0.f;
+    const bool last = st.meta & 1;
+    if (!last) read_x((nx.meta >> 1) & 7);  // same unit: its x is in LDS already
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int gs = 0; gs < GSUB; ++gs) {
+        const half4_t sh = __builtin_bit_cast(half4_t, st.sc[r][gs]);
+        float4_t part = {0.f, 0.f, 0.f, 0.f};
+        if (BIAS) {
+#pragma unroll
+          for (int mm = 0; mm < MPG; ++mm)
+            part = mfma16x16x32(magic8r(lane_dword(st.w[r], gs * MPG + mm), dq), xc[gs * MPG + mm], part);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf((float)sh[i], part[i] - bc[gs], acc[r][i]);
+        } else {
+          const _Float16 z = (_Float16)(float)st.z[r][gs];
+          const half2_t blo = {(_Float16)-1024.0f - z, (_Float16)-1024.0f - z};
+          const half2_t bhi = {(_Float16)-64.0f - z, (_Float16)-64.0f - z};
+#pragma unroll
+          for (int mm = 0; mm < MPG; ++mm)
+            part = mfma16x16x32(dequant8r(lane_dword(st.w[r], gs * MPG + mm), dq, blo, bhi), xc[gs * MPG + mm], part);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf((float)sh[i], part[i], acc[r][i]);
+        }
+      }
+    }
+    if (!last) return;
+    if (real_col) {
+      float* pp = part0 + (size_t)(st.meta >> 4) * R * 16 * B + bcol * 16 + crow;
+#pragma unroll
+      for (int r = 0; r < R; ++r) *reinterpret_cast<float4_t*>(pp + r * 16 * B) = acc[r];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // the next unit: its x replaces this one's in LDS (this unit's reads of it were
+    // issued earlier by this wavefront, and LDS serves them in order)
+    if (nx.meta >= 0) write_x();
+    read_x(0);
+  };
+
+  while (buf[0].meta >= 0) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      load(buf[(p + P - 1) % P]);
+      if (buf[p].meta >= 0) compute(buf[p], buf[(p + 1) % P]);
+    }
+  }
+
+  // results: the units' partials added in chunk order -> y
+  lds_barrier();
+  const int nout = n_rb * R * 16 * B;
+  for (int e = threadIdx.x; e < nout; e += blockDim.x) {
+    const int row = e & 15;
+    const int t = e >> 4;
+    const int b = t % B;
+    const int ir = t / B;  // i * R + r
+    const int i = ir / R, r = ir - i * R;
+    const float* pp = part0 + ((size_t)i * CH * R + r) * 16 * B + b * 16 + row;
+    float sum = 0.f;
+    for (int c = 0; c < CH; ++c) sum += pp[(size_t)c * R * 16 * B];
+    const int n = ((rb_first + i * rb_stride) * R + r) * 16 + row;
+    if (n < N) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
 // Resident workgroups per CU for a kernel / block / LDS combination, and the CU
 // count of the current device; both are fixed for a process, so they are looked
 // up once and remembered.
@@ -472,7 +755,58 @@ hipError_t launch_gemv_a(const GemmArgs& a, hipStream_t stream) {
   return a.asym ? launch_gemv_g<R, true>(a, stream) : launch_gemv_g<R, false>(a, stream);
 }
 
+template <int R, int GSUB, bool ASYM>
+hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
+  constexpr int BMAX = 1;
+  constexpr int P = R == 1 ? 8 : 4;
+  const int T = a.Np / kTileRows;
+  const int S = a.Kp / kSuperK;
+  const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
+  const int W = std::min(a.waves_per_group, 8);
+  const int nRB = (T + R - 1) / R;
+  const int CH = S / kUnitBlocks;
+  const void* fn = reinterpret_cast<const void*>(&gemv_stream_kernel<R, GSUB, ASYM, P>);
+  const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
+  const size_t base = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, 0).total;
+  const size_t lim = std::max(a.lds_limit, base + unit_bytes * CH);
+  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, base + unit_bytes * CH) * device_cus();
+  int64_t grid = std::max<int64_t>(1, std::min<int64_t>(nRB, resident));
+  if (a.grid_limit > 0) grid = std::min<int64_t>(grid, a.grid_limit);
+  int n_rb = (int)((nRB + grid - 1) / grid);
+  const int64_t max_rb = std::max<int64_t>(1, (int64_t)((lim - base) / (unit_bytes * CH)));
+  if (n_rb > max_rb) grid = (nRB + max_rb - 1) / max_rb;
+  n_rb = (int)((nRB + grid - 1) / grid);
+  const size_t lds = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, n_rb * CH).total;
+  hipLaunchKernelGGL((gemv_stream_kernel<R, GSUB, ASYM, P>), dim3((unsigned)grid), dim3(W * kWave), lds,
+                     stream, static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
+                     static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
+                     a.Gp, J, nRB, static_cast<uint16_t*>(a.y));
+  return hipGetLastError();
+}
+
+template <int R, bool ASYM>
+hipError_t launch_gemv_stream_g(const GemmArgs& a, hipStream_t stream) {
+  if (a.group == 32) return launch_gemv_stream_t<R, 4, ASYM>(a, stream);
+  if (a.group == 64) return launch_gemv_stream_t<R, 2, ASYM>(a, stream);
+  return launch_gemv_stream_t<R, 1, ASYM>(a, stream);
+}
+
+template <int R>
+hipError_t launch_gemv_stream_a(const GemmArgs& a, hipStream_t stream) {
+  return a.asym ? launch_gemv_stream_g<R, true>(a, stream) : launch_gemv_stream_g<R, false>(a, stream);
+}
+
+}  // namespace
+
+bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
+  const int S = Kp / kSuperK;
+  return B == 1 && k_splits == 1 && rows_per_wave == 2 && S % kUnitBlocks == 0;
+}
+
+namespace {
+
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
+  if (gemv_streams_x(a.B, a.Kp, a.rows_per_wave, a.k_splits)) return launch_gemv_stream_a<2>(a, stream);
   switch (a.rows_per_wave) {
     case 1: return launch_gemv_a<1>(a, stream);
     case 2: return launch_gemv_a<2>(a, stream);

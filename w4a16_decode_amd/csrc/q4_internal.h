@@ -55,5 +55,8 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Whether the GEMV for this shape streams x per unit (B = 1, one split, two row tiles
+// per wavefront, a multiple of 1024 channels) instead of staging the whole slice.
+bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits);
 
 }  // namespace q4
