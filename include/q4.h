@@ -115,8 +115,8 @@ q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t 
                                 void* packed, void* scales, void* zeros, void* stream);
 
 /* Bytes of device workspace q4_gemm / q4_gemm_asym need for this shape: float32
- * partial sums when the channel range is split over several workgroups (B <= 16
- * with a long `in`, or too few rows to fill the GPU); 0 when none is needed. The
+ * partial sums when the channel range is split over several workgroups (a long
+ * `in` with B <= 16, or too few rows to fill the GPU); 0 when none is needed. The
  * workspace is scratch: its contents on entry are ignored and undefined on return. */
 size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group);
 
@@ -149,9 +149,11 @@ q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void*
  *   one split must fit the device's LDS per workgroup. Needs
  *   k_splits * B * out * 4 bytes of workspace when k_splits > 1.
  * B > 16 (skinny GEMM): `rows_per_wave` 1, 2 or 4, `waves_per_group` 4,
- *   `k_splits` 1, `col_tiles` 2, 4 or 8 tiles of 16 batch rows per workgroup,
- *   with rows_per_wave * col_tiles * max(1, 128 / group) <= 16 (accumulator
- *   registers); no workspace. */
+ *   `col_tiles` 2, 4 or 8 tiles of 16 batch rows per workgroup, with
+ *   rows_per_wave * col_tiles * max(1, 128 / group) <= 16 (accumulator
+ *   registers), `k_splits` workgroups splitting the channel range in chunks of
+ *   16 / col_tiles blocks of 128 (at most as many splits as chunks). Needs
+ *   k_splits * B * out * 4 bytes of workspace when k_splits > 1. */
 q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales,
                          const void* zeros, int32_t asym, int64_t out, int64_t in, int32_t group,
                          void* y, int32_t rows_per_wave, int32_t waves_per_group, int32_t k_splits,

@@ -113,15 +113,19 @@ bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, siz
 }
 
 // LDS of one skinny-GEMM workgroup: two activation tiles of col_tiles * 16 rows x
-// 136 halfs (128 channels + a 16-byte pad against bank conflicts).
-size_t mfma_lds(int col_tiles) { return (size_t)2 * col_tiles * 16 * 136 * 2; }
+// (16 / col_tiles) * 128 channels, each row padded by 16 bytes (mfma_chunk_blocks in
+// q4_gemm.hip).
+size_t mfma_lds(int col_tiles) { return (size_t)2 * col_tiles * 16 * ((16 / col_tiles) * 128 + 8) * 2; }
 
-// Register budget of the skinny GEMM: R x CT accumulator tiles and one partial tile
-// per group of a 128-channel block.
-bool mfma_shape_ok(int R, int W, int KS, int CT, int group) {
-  if (W != 4 || KS != 1) return false;
+// Skinny GEMM launch shapes: R x CT accumulator tiles and one partial tile per
+// group of a 128-channel block must fit the registers, the two activation tiles
+// the LDS, and every k-split must get at least one chunk of 16 / CT blocks.
+bool mfma_shape_ok(int R, int W, int KS, int CT, int group, int S) {
+  if (W != 4) return false;
   if (R != 1 && R != 2 && R != 4) return false;
   if (CT != 2 && CT != 4 && CT != 8) return false;
+  const int chunks = (S + 16 / CT - 1) / (16 / CT);
+  if (KS < 1 || KS > chunks) return false;
   const int gsub = group >= 128 ? 1 : 128 / group;
   return R * CT * gsub <= 16 && mfma_lds(CT) <= lds_per_block();
 }
@@ -150,18 +154,24 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     return;
   }
   // B > 16: skinny MFMA GEMM, 4 wavefronts per workgroup, CT column tiles of 16
-  // per workgroup (double-buffered activation tile in LDS), R row tiles per wavefront
-  int CT = col_tiles_total <= 2 ? 2 : (col_tiles_total <= 4 ? 4 : 8);
-  int R = (B <= 64 || T < 1024) ? 1 : 2;
-  while (!mfma_shape_ok(R, 4, 1, CT, d.group)) {
+  // per workgroup (double-buffered activation tiles in LDS), R row tiles per
+  // wavefront; 2 column tiles up to B = 32, else 4; 4 row tiles from B = 128 on
+  // (compute-bound), else 2; k-splits (floor(256 / workgroups)) for matrices with
+  // too few row tiles to give every CU a workgroup.
+  int CT = col_tiles_total <= 2 ? 2 : 4;
+  int R = B >= 128 ? 4 : 2;
+  while (!mfma_shape_ok(R, 4, 1, CT, d.group, S)) {
     if (R > 1) R /= 2;
     else if (CT > 2) CT /= 2;
     else break;  // unreachable: R = 1, CT = 2 always fits
   }
+  const int64_t wgs = (int64_t)((T + 4 * R - 1) / (4 * R)) * ((col_tiles_total + CT - 1) / CT);
+  int KS = (int)std::min<int64_t>(8, std::max<int64_t>(1, 256 / wgs));
+  while (KS > 1 && !mfma_shape_ok(R, 4, KS, CT, d.group, S)) --KS;
   a->col_tiles = CT;
   a->rows_per_wave = R;
   a->waves_per_group = 4;
-  a->k_splits = 1;
+  a->k_splits = KS;
 }
 
 size_t splits_workspace(const q4::GemmArgs& a) {
@@ -277,9 +287,10 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
         return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: more splits than 128-channel blocks, "
                     "or the activation slice of B=%lld does not fit LDS or the copy",
                     (int)k_splits, (int)waves_per_group, (long long)B);
-    } else if (!mfma_shape_ok(rows_per_wave, waves_per_group, k_splits, col_tiles, d.group)) {
-      return fail(Q4_ERR_UNSUPPORTED, "for B > 16: waves_per_group must be 4, k_splits 1, col_tiles 2, 4 or 8 "
-                  "(within LDS), rows_per_wave * col_tiles * max(1, 128 / group) <= 16");
+    } else if (!mfma_shape_ok(rows_per_wave, waves_per_group, k_splits, col_tiles, d.group, d.Kp / 128)) {
+      return fail(Q4_ERR_UNSUPPORTED, "for B > 16: waves_per_group must be 4, col_tiles 2, 4 or 8 (within LDS), "
+                  "rows_per_wave * col_tiles * max(1, 128 / group) <= 16, k_splits at most the chunks of "
+                  "16 / col_tiles blocks");
     }
     a.col_tiles = col_tiles;
     a.rows_per_wave = rows_per_wave;

@@ -821,14 +821,13 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
 // the workgroup owns column tiles CT*blockIdx.y .. + CT - 1 (16 batch rows each).
 // Codes are dequantized exactly to float16 integers (q, or q - z) in registers, as
 // in the GEMV; each group's MFMA partial sum is scaled in float32 and added to the
-// accumulator tile. The activation tile of each 128-channel step (CT*16 rows x 128
-// channels) is staged in double-buffered, padded LDS and read by the four
-// wavefronts as B operands, each read feeding RT row tiles. Codes/scales are
-// prefetched PW steps ahead; the next step's activation tile is loaded into
-// registers before the current step's MFMAs and written to the other LDS buffer
-// after them.
-constexpr int kXRow = kSuperK + 8;  // halfs per LDS row of the activation tile (16-byte pad)
-
+// accumulator tile. The channel range is walked in chunks of NB blocks (NB * 128
+// channels): the chunk's activation tile (CT*16 rows) sits in one of two padded
+// LDS buffers and is read by the four wavefronts as B operands, each read feeding
+// RT row tiles. The next chunk's tile is loaded into registers a whole chunk ahead
+// and written to the other buffer at the chunk's end, so there is one barrier per
+// chunk; codes and scales stream through a ring of NB stages (NB - 1 blocks in
+// flight) that runs on across chunk boundaries.
 template <int RT, int GSUB, bool ASYM>
 struct GStage {
   uint4 w[RT];
@@ -836,29 +835,39 @@ struct GStage {
   uint32_t z[RT][GSUB];  // zero point of the lane's A-operand row per group (asymmetric)
 };
 
-template <int RT, int CT, int GSUB, bool ASYM, int PW>
+template <int RT, int CT, int GSUB, bool ASYM, int NB>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restrict__ x, int B,
                                                         const uint4* __restrict__ packed,
                                                         const uint16_t* __restrict__ scales,
                                                         const uint8_t* __restrict__ zeros, int N, int K, int T,
-                                                        int S, int Gp, int J, uint16_t* __restrict__ y) {
+                                                        int S, int Gp, int J, uint16_t* __restrict__ y,
+                                                        float* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MPG = 4 / GSUB;
   constexpr int XROWS = CT * 16;
-  constexpr int XCH = XROWS * 16 / 256;  // 16-byte chunks of one activation tile per thread
-  uint16_t* xbuf = reinterpret_cast<uint16_t*>(smem);  // [2][XROWS][kXRow]
+  constexpr int KC = NB * kSuperK;           // channels per chunk
+  constexpr int XSTR = KC + 8;               // halfs per LDS row (16-byte pad against bank conflicts)
+  constexpr int C8 = KC / 8;                 // 16-byte pieces per row of a chunk
+  constexpr int XCH = XROWS * C8 / 256;      // pieces of one chunk's tile per thread
+  uint16_t* xbuf = reinterpret_cast<uint16_t*>(smem);  // [2][XROWS][XSTR]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, arow = lane & 15, crow = 4 * (lane >> 4);
   const int tile0 = blockIdx.x * 4 * RT + wave * RT;
   const int b0 = blockIdx.y * XROWS;
+  // k-split blockIdx.z of gridDim.z: whole chunks [c0, c0 + nchunks) of the channel range
+  const int all_chunks = (S + NB - 1) / NB;
+  const int KS = gridDim.z, ks = blockIdx.z;
+  const int c0 = (int)(((int64_t)all_chunks * ks) / KS);
+  const int nchunks = (int)(((int64_t)all_chunks * (ks + 1)) / KS) - c0;  // >= 1: the host keeps KS <= chunks
+  const int S1 = min(S, (c0 + nchunks) * NB);  // end of this split's blocks
 
   int tiles[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) tiles[r] = min(tile0 + r, T - 1);
 
-  auto load_w = [&](GStage<RT, GSUB, ASYM>& st, int s) {
-    s = min(s, S - 1);  // trailing prefetches re-read the last block: no branch around loads
+  auto load_w = [&](GStage<RT, GSUB, ASYM>& st, int s) __attribute__((always_inline)) {
+    s = min(c0 * NB + s, S1 - 1);  // trailing prefetches re-read the last block: no branch around loads
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const uint4* wp = packed + ((size_t)tiles[r] * S + s) * kWave + lane;
@@ -872,24 +881,25 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
       }
     }
   };
-  // this thread's chunks of an activation tile: chunk c = threadIdx.x + 256 * i -> row c / 16, 8 halfs at 8 * (c % 16)
-  auto load_x = [&](uint4 (&v)[XCH], int s) {
-    s = min(s, S - 1);
+  // this thread's pieces of a chunk's activation tile: piece i = threadIdx.x + 256 * i
+  // -> row i / C8, 8 halfs at 8 * (i % C8) of the chunk
+  auto load_x = [&](uint4 (&v)[XCH], int c) __attribute__((always_inline)) {
+    c = c0 + min(c, nchunks - 1);
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int b = min(b0 + (c >> 4), B - 1);
-      const int k = min(s * kSuperK + 8 * (c & 15), K - 8);
+      const int pc = threadIdx.x + 256 * i;
+      const int b = min(b0 + pc / C8, B - 1);
+      const int k = min(c * KC + 8 * (pc % C8), K - 8);
       v[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
     }
   };
-  auto store_x = [&](const uint4 (&v)[XCH], int s, int buf) {
+  auto store_x = [&](const uint4 (&v)[XCH], int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c >> 4, col = 8 * (c & 15);
-      const bool valid = (b0 + row < B) && (s * kSuperK + col < K);
-      *reinterpret_cast<uint4*>(xbuf + (buf * XROWS + row) * kXRow + col) = valid ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+      const int pc = threadIdx.x + 256 * i;
+      const int row = pc / C8, col = 8 * (pc % C8);
+      const bool valid = (b0 + row < B) && ((c0 + c) * KC + col < K);
+      *reinterpret_cast<uint4*>(xbuf + (buf * XROWS + row) * XSTR + col) = valid ? v[i] : make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
@@ -901,18 +911,17 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
 
   uint4 xv[XCH];
   load_x(xv, 0);
-  GStage<RT, GSUB, ASYM> ring[PW];
+  GStage<RT, GSUB, ASYM> ring[NB];
 #pragma unroll
-  for (int p = 0; p < PW; ++p) load_w(ring[p], p);
+  for (int p = 0; p < NB - 1; ++p) load_w(ring[p], p);
   store_x(xv, 0, 0);
   lds_barrier();
+  load_x(xv, 1);  // a whole chunk ahead
 
   const DequantRegs dq = DequantRegs::make();
 
-  auto step = [&](GStage<RT, GSUB, ASYM>& st, int s) {
-    const int buf = s & 1;
-    load_x(xv, s + 1);  // next activation tile: issued before the next codes (in-order completion)
-    // this block's codes as float16 integers in MFMA A-operand order, and the scales
+  // block p of the chunk in buffer buf, codes from stage st
+  auto step = [&](const GStage<RT, GSUB, ASYM>& st, int buf, int p) __attribute__((always_inline)) {
     half8_t a[RT][4];
     float4_t sc[RT][GSUB];
 #pragma unroll
@@ -930,13 +939,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
         for (int i = 0; i < 4; ++i) sc[r][gs][i] = (float)sh[i];
       }
     }
-    load_w(st, s + PW);  // codes for PW steps ahead into the slot just consumed
-    const uint16_t* xb = xbuf + (buf * XROWS + (lane & 15)) * kXRow + 8 * kq;
+    const uint16_t* xb = xbuf + (buf * XROWS + (lane & 15)) * XSTR + p * kSuperK + 8 * kq;
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       half8_t bop[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) bop[m] = *reinterpret_cast<const half8_t*>(xb + c * 16 * kXRow + m * kBlockK);
+      for (int m = 0; m < 4; ++m) bop[m] = *reinterpret_cast<const half8_t*>(xb + c * 16 * XSTR + m * kBlockK);
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
 #pragma unroll
@@ -949,14 +957,21 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
         }
       }
     }
-    store_x(xv, s + 1, buf ^ 1);  // the other buffer was last read in step s-1, before the barrier
-    lds_barrier();
   };
 
-  for (int s = 0; s < S; s += PW) {
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
 #pragma unroll
-    for (int p = 0; p < PW; ++p)
-      if (s + p < S) step(ring[p], s + p);
+    for (int p = 0; p < NB; ++p) {
+      const int s = c * NB + p;  // block of this split
+      load_w(ring[(p + NB - 1) % NB], s + NB - 1);  // into the slot of block s - 1
+      if (c0 * NB + s < S1) step(ring[p], buf, p);
+    }
+    // the next chunk's tile into the other buffer (last read in chunk c - 1, before
+    // the previous barrier), then the one after that into registers
+    store_x(xv, c + 1, buf ^ 1);
+    lds_barrier();
+    load_x(xv, c + 2);
   }
 
   // accumulator element i of lane l in tile (r, c): row 16*tile + crow + i, batch row b0 + 16c + l%16
@@ -970,25 +985,40 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = (tile0 + r) * 16 + crow + i;
-        if (n < N) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[r][c][i]);
+        if (n >= N) continue;
+        if (KS == 1) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[r][c][i]);
+        else ws[((size_t)ks * B + b) * N + n] = acc[r][c][i];
       }
     }
   }
 }
 
+// Blocks per chunk: the LDS of the two activation buffers stays at about 66 KiB
+// (two workgroups per CU) whatever the column tiles.
+template <int CT>
+constexpr int mfma_chunk_blocks() { return 16 / CT; }
+
 template <int RT, int CT, int GSUB, bool ASYM>
 hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
-  constexpr int PW = 3;
+  constexpr int NB = mfma_chunk_blocks<CT>();
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
   const int col_tiles = (a.B + 15) / 16;
-  dim3 grid((T + 4 * RT - 1) / (4 * RT), (col_tiles + CT - 1) / CT);
-  const size_t lds = (size_t)2 * CT * 16 * kXRow * 2;
-  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, PW>), grid, dim3(256), lds, stream,
+  const int KS = a.k_splits;
+  dim3 grid((T + 4 * RT - 1) / (4 * RT), (col_tiles + CT - 1) / CT, KS);
+  const size_t lds = (size_t)2 * CT * 16 * (NB * kSuperK + 8) * 2;
+  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, NB>), grid, dim3(256), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
-                     a.Gp, J, static_cast<uint16_t*>(a.y));
+                     a.Gp, J, static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
+  if (KS > 1) {
+    const int64_t BN = (int64_t)a.B * a.N;
+    int64_t blocks = (BN + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const float*>(a.workspace), KS, BN, static_cast<uint16_t*>(a.y));
+  }
   return hipGetLastError();
 }
 

@@ -183,7 +183,7 @@ def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int
     lib = _lib.load()
     if col_tiles is None:
         col_tiles = 1 if B <= 16 else min(8, max(2, 1 << ((B + 15) // 16 - 1).bit_length()))
-    need = 4 * k_splits * B * qw.out_features if (k_splits > 1 and B <= 16) else 0
+    need = 4 * k_splits * B * qw.out_features if k_splits > 1 else 0
     ws_ptr, ws_bytes = _workspace(x, need, workspace)
     st = lib.q4_gemm_config(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(),
                             qw.zeros.data_ptr() if qw.zeros is not None else None, int(qw.asym),
