@@ -148,7 +148,8 @@ q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void*
  *   splitting the channel range, `col_tiles` must be 1. The activation slice of
  *   one split must fit the device's LDS per workgroup. Needs
  *   k_splits * B * out * 4 bytes of workspace when k_splits > 1.
- * B > 16 (skinny GEMM): `rows_per_wave` 1, 2 or 4, `waves_per_group` 4,
+ * B > 16 (skinny GEMM): `rows_per_wave` 1, 2 or 4, `waves_per_group` 4 or 8
+ *   (8 only with rows_per_wave <= 2),
  *   `col_tiles` 2, 4 or 8 tiles of 16 batch rows per workgroup, with
  *   rows_per_wave * col_tiles * max(1, 128 / group) <= 16 (accumulator
  *   registers), `k_splits` workgroups splitting the channel range in chunks of

@@ -121,7 +121,8 @@ size_t mfma_lds(int col_tiles) { return (size_t)2 * col_tiles * 16 * ((16 / col_
 // group of a 128-channel block must fit the registers, the two activation tiles
 // the LDS, and every k-split must get at least one chunk of 16 / CT blocks.
 bool mfma_shape_ok(int R, int W, int KS, int CT, int group, int S) {
-  if (W != 4) return false;
+  if (W != 4 && W != 8) return false;
+  if (W == 8 && R > 2) return false;
   if (R != 1 && R != 2 && R != 4) return false;
   if (CT != 2 && CT != 4 && CT != 8) return false;
   const int chunks = (S + 16 / CT - 1) / (16 / CT);
@@ -139,9 +140,11 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     // stay resident per CU)
     const size_t lim = lds_per_block();
     a->col_tiles = 1;
-    // one row tile per wavefront, two for square-ish matrices with few tiles (the
-    // extra tile per load keeps more bytes in flight where there are few row blocks)
-    const int R = (T >= 2048 || d.group < 128 || T > S * 8) ? 1 : 2;
+    // two row tiles per wavefront for square-ish matrices of 512 to 2047 tiles (the
+    // extra tile per load keeps more bytes in flight where there are few row
+    // blocks), else one: tall matrices, small groups (several scales per block) and
+    // matrices so small that two tiles per row block would leave CUs idle
+    const int R = (T >= 2048 || d.group < 128 || T > S * 8 || T < 512) ? 1 : 2;
     // 8 wavefronts (two workgroups per CU) stream best for B <= 4; 16 hold twice
     // the activation slice, which keeps larger batches from splitting the channels
     const int W = B <= 4 ? 8 : gemv_max_waves(R, d.group);
@@ -153,24 +156,25 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     a->lds_limit = lim;
     return;
   }
-  // B > 16: skinny MFMA GEMM, 4 wavefronts per workgroup, CT column tiles of 16
-  // per workgroup (double-buffered activation tiles in LDS), R row tiles per
-  // wavefront; 2 column tiles up to B = 32, else 4; 4 row tiles from B = 128 on
-  // (compute-bound), else 2; k-splits (floor(256 / workgroups)) for matrices with
-  // too few row tiles to give every CU a workgroup.
-  int CT = col_tiles_total <= 2 ? 2 : 4;
-  int R = B >= 128 ? 4 : 2;
-  while (!mfma_shape_ok(R, 4, 1, CT, d.group, S)) {
+  // B > 16: skinny MFMA GEMM, 8 wavefronts per workgroup sharing CT column tiles of
+  // 16 batch rows (double-buffered activation chunks in LDS): 2 column tiles up to
+  // B = 32, 4 up to 128, else 8; 2 row tiles per wavefront; the channel range split
+  // over up to 4 workgroups until there are about 256 of them, with 1 row tile per
+  // wavefront when even that leaves too few. (Measured on the Llama-3-70B shapes.)
+  int CT = col_tiles_total <= 2 ? 2 : (col_tiles_total <= 8 ? 4 : 8);
+  int R = 2;
+  auto wgs = [&](int r) { return (int64_t)((T + 8 * r - 1) / (8 * r)) * ((col_tiles_total + CT - 1) / CT); };
+  if (256 / wgs(R) > 4) R = 1;
+  while (!mfma_shape_ok(R, 8, 1, CT, d.group, S)) {
     if (R > 1) R /= 2;
     else if (CT > 2) CT /= 2;
     else break;  // unreachable: R = 1, CT = 2 always fits
   }
-  const int64_t wgs = (int64_t)((T + 4 * R - 1) / (4 * R)) * ((col_tiles_total + CT - 1) / CT);
-  int KS = (int)std::min<int64_t>(8, std::max<int64_t>(1, 256 / wgs));
-  while (KS > 1 && !mfma_shape_ok(R, 4, KS, CT, d.group, S)) --KS;
+  int KS = (int)std::min<int64_t>(4, std::max<int64_t>(1, 256 / wgs(R)));
+  while (KS > 1 && !mfma_shape_ok(R, 8, KS, CT, d.group, S)) --KS;
   a->col_tiles = CT;
   a->rows_per_wave = R;
-  a->waves_per_group = 4;
+  a->waves_per_group = 8;
   a->k_splits = KS;
 }
 
@@ -288,7 +292,8 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
                     "or the activation slice of B=%lld does not fit LDS or the copy",
                     (int)k_splits, (int)waves_per_group, (long long)B);
     } else if (!mfma_shape_ok(rows_per_wave, waves_per_group, k_splits, col_tiles, d.group, d.Kp / 128)) {
-      return fail(Q4_ERR_UNSUPPORTED, "for B > 16: waves_per_group must be 4, col_tiles 2, 4 or 8 (within LDS), "
+      return fail(Q4_ERR_UNSUPPORTED, "for B > 16: waves_per_group must be 4 or 8 (8 only with rows_per_wave <= 2), "
+                  "col_tiles 2, 4 or 8 (within LDS), "
                   "rows_per_wave * col_tiles * max(1, 128 / group) <= 16, k_splits at most the chunks of "
                   "16 / col_tiles blocks");
     }

@@ -817,13 +817,13 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------------
 // Skinny GEMM for B > 16 (MFMA-bound from a few dozen rows of x upward).
 //
-// Workgroup = 4 wavefronts; wavefront w owns row tiles 4*RT*blockIdx.x + RT*w + r,
+// Workgroup = WV (4 or 8) wavefronts; wavefront w owns row tiles WV*RT*blockIdx.x + RT*w + r,
 // the workgroup owns column tiles CT*blockIdx.y .. + CT - 1 (16 batch rows each).
 // Codes are dequantized exactly to float16 integers (q, or q - z) in registers, as
 // in the GEMV; each group's MFMA partial sum is scaled in float32 and added to the
 // accumulator tile. The channel range is walked in chunks of NB blocks (NB * 128
 // channels): the chunk's activation tile (CT*16 rows) sits in one of two padded
-// LDS buffers and is read by the four wavefronts as B operands, each read feeding
+// LDS buffers and is read by all wavefronts as B operands, each read feeding
 // RT row tiles. The next chunk's tile is loaded into registers a whole chunk ahead
 // and written to the other buffer at the chunk's end, so there is one barrier per
 // chunk; codes and scales stream through a ring of NB stages (NB - 1 blocks in
@@ -835,8 +835,8 @@ struct GStage {
   uint32_t z[RT][GSUB];  // zero point of the lane's A-operand row per group (asymmetric)
 };
 
-template <int RT, int CT, int GSUB, bool ASYM, int NB>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restrict__ x, int B,
+template <int RT, int CT, int GSUB, bool ASYM, int NB, int WV>
+__global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __restrict__ x, int B,
                                                         const uint4* __restrict__ packed,
                                                         const uint16_t* __restrict__ scales,
                                                         const uint8_t* __restrict__ zeros, int N, int K, int T,
@@ -848,12 +848,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
   constexpr int KC = NB * kSuperK;           // channels per chunk
   constexpr int XSTR = KC + 8;               // halfs per LDS row (16-byte pad against bank conflicts)
   constexpr int C8 = KC / 8;                 // 16-byte pieces per row of a chunk
-  constexpr int XCH = XROWS * C8 / 256;      // pieces of one chunk's tile per thread
+  constexpr int NT = WV * 64;                // threads
+  constexpr int XCH = XROWS * C8 / NT;       // pieces of one chunk's tile per thread
   uint16_t* xbuf = reinterpret_cast<uint16_t*>(smem);  // [2][XROWS][XSTR]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, arow = lane & 15, crow = 4 * (lane >> 4);
-  const int tile0 = blockIdx.x * 4 * RT + wave * RT;
+  const int tile0 = blockIdx.x * WV * RT + wave * RT;
   const int b0 = blockIdx.y * XROWS;
   // k-split blockIdx.z of gridDim.z: whole chunks [c0, c0 + nchunks) of the channel range
   const int all_chunks = (S + NB - 1) / NB;
@@ -881,13 +882,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
       }
     }
   };
-  // this thread's pieces of a chunk's activation tile: piece i = threadIdx.x + 256 * i
+  // this thread's pieces of a chunk's activation tile: piece i = threadIdx.x + NT * i
   // -> row i / C8, 8 halfs at 8 * (i % C8) of the chunk
   auto load_x = [&](uint4 (&v)[XCH], int c) __attribute__((always_inline)) {
     c = c0 + min(c, nchunks - 1);
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int pc = threadIdx.x + 256 * i;
+      const int pc = threadIdx.x + NT * i;
       const int b = min(b0 + pc / C8, B - 1);
       const int k = min(c * KC + 8 * (pc % C8), K - 8);
       v[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
@@ -896,7 +897,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
   auto store_x = [&](const uint4 (&v)[XCH], int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int pc = threadIdx.x + 256 * i;
+      const int pc = threadIdx.x + NT * i;
       const int row = pc / C8, col = 8 * (pc % C8);
       const bool valid = (b0 + row < B) && ((c0 + c) * KC + col < K);
       *reinterpret_cast<uint4*>(xbuf + (buf * XROWS + row) * XSTR + col) = valid ? v[i] : make_uint4(0u, 0u, 0u, 0u);
@@ -993,12 +994,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restri
   }
 }
 
-// Blocks per chunk: the LDS of the two activation buffers stays at about 66 KiB
-// (two workgroups per CU) whatever the column tiles.
+// Blocks per chunk: the two activation buffers take about 132 KiB of LDS (one
+// workgroup per CU) whatever the column tiles.
 template <int CT>
 constexpr int mfma_chunk_blocks() { return 16 / CT; }
 
-template <int RT, int CT, int GSUB, bool ASYM>
+template <int RT, int CT, int GSUB, bool ASYM, int WV>
 hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
   constexpr int NB = mfma_chunk_blocks<CT>();
   const int T = a.Np / kTileRows;
@@ -1006,9 +1007,9 @@ hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
   const int col_tiles = (a.B + 15) / 16;
   const int KS = a.k_splits;
-  dim3 grid((T + 4 * RT - 1) / (4 * RT), (col_tiles + CT - 1) / CT, KS);
+  dim3 grid((T + WV * RT - 1) / (WV * RT), (col_tiles + CT - 1) / CT, KS);
   const size_t lds = (size_t)2 * CT * 16 * (NB * kSuperK + 8) * 2;
-  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, NB>), grid, dim3(256), lds, stream,
+  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, NB, WV>), grid, dim3(WV * 64), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
                      a.Gp, J, static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
@@ -1023,10 +1024,16 @@ hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
 }
 
 // Only shapes whose accumulators and per-group partial tiles fit the register file
-// (RT * CT * GSUB <= 16) are built; the host never selects the others.
+// (RT * CT * GSUB <= 16, and RT <= 2 with 8 wavefronts) are built; the host never
+// selects the others.
 template <int RT, int CT, int GSUB, bool ASYM>
 hipError_t launch_mfma_fit(const GemmArgs& a, hipStream_t stream) {
-  if constexpr (RT * CT * GSUB <= 16) return launch_mfma_t<RT, CT, GSUB, ASYM>(a, stream);
+  if constexpr (RT * CT * GSUB <= 16) {
+    if constexpr (RT <= 2) {  // 8 wavefronts: at most 256 VGPRs each
+      if (a.waves_per_group == 8) return launch_mfma_t<RT, CT, GSUB, ASYM, 8>(a, stream);
+    }
+    return launch_mfma_t<RT, CT, GSUB, ASYM, 4>(a, stream);
+  }
   return hipErrorInvalidConfiguration;
 }
 
