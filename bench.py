@@ -10,7 +10,8 @@ the algorithmic bytes: packed codes + float16 scales + float16 activations
 The same line carries:
   roofline      the dominant kernel (the fused gate/up GEMV, 55% of the bytes)
                 against the 8 TB/s HBM peak; its average duration is measured
-                with HIP events on its stream inside this run. `traffic` comes
+                with HIP events on its stream inside this run (the 80 layers'
+                gate/up launches back to back in a HIP graph). `traffic` comes
                 from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary under profiles/
                 when that was taken on the current kernel sources, else null.
   cpu_baseline  the CPU oracle (numpy float64) timed on a bounded sample of the
@@ -22,7 +23,8 @@ The same line carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 Profiling helpers: --only-kernel {gate_up,down,qkv,o} [--reps N] runs just that
-GEMV kind of a few 70B layers; --copy-calibration runs a 256 MiB device copy.
+GEMV kind of a few 70B layers; --only-batch B [--reps N] runs the product on one
+28672x8192 matrix at batch B; --copy-calibration runs a 256 MiB device copy.
 """
 
 from __future__ import annotations
@@ -162,28 +164,16 @@ class Sweep:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / 1e3 / steps
 
-    def time_kernel(self, pick: str, reps: int = 2):
-        """Per-launch duration of the launches named `pick`, HIP events on their stream."""
-        import torch
-
+    def time_kernel(self, pick: str, reps: int = 5):
+        """Average duration of the launches named `pick` (one per layer, back to back in a
+        HIP graph, so every launch streams a different layer's weights from HBM), from
+        HIP events on the stream they run on. Returns (seconds, a QuantizedWeight of
+        that kind, launches timed)."""
         import w4a16_decode_amd as q4
 
-        stream = torch.cuda.current_stream()
-        durs = []
-        for _ in range(reps):
-            evs = []
-            for name, x, qw, y in self.launches():
-                if name == pick:
-                    a, b = events()
-                    a.record(stream)
-                    q4.gemm(x, qw, out=y, workspace=self.ws)
-                    b.record(stream)
-                    evs.append((a, b, qw))
-                else:
-                    q4.gemm(x, qw, out=y, workspace=self.ws)
-            torch.cuda.synchronize()
-            durs += [(a.elapsed_time(b) / 1e3, qw) for a, b, qw in evs]
-        return durs
+        picked = [(x, qw, y) for name, x, qw, y in self.launches() if name == pick]
+        t = graph_time(lambda: [q4.gemm(x, qw, out=y, workspace=self.ws) for x, qw, y in picked], reps)
+        return t / len(picked), picked[0][1], len(picked) * reps
 
 
 def recorded_traffic():
@@ -346,6 +336,24 @@ def only_kernel(kind: str, reps: int, layers: int, dev, group: int):
     log(f"[bench] ran {kind} x {reps * len(picked)}")
 
 
+def only_batch(B: int, reps: int, dev, group: int):
+    """Run the W4A16 product on one 28672x8192 matrix at batch B, for counter collection."""
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+
+    N, K = 28672, 8192
+    qw = q4.quantize_pack(synth.device_weight(N, K, seed=4, layer=0, matrix=0, device=dev), group)
+    x = synth.device_activation(B, K, seed=4, layer=0, matrix=0, device=dev)
+    y = torch.empty((B, N), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(16, q4.workspace_bytes(B, N, K, group)), dtype=torch.uint8, device=dev)
+    for _ in range(reps):
+        q4.gemm(x, qw, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] ran 28672x8192 B={B} x {reps}")
+
+
 def copy_calibration(dev):
     import torch
 
@@ -366,6 +374,7 @@ def main(argv=None):
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-kernel", choices=["gate_up", "down", "qkv", "o"])
+    ap.add_argument("--only-batch", type=int, default=0)
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -391,6 +400,9 @@ def main(argv=None):
     if args.only_kernel:
         only_kernel(args.only_kernel, args.reps, min(args.layers, 4), dev, group)
         return 0
+    if args.only_batch:
+        only_batch(args.only_batch, args.reps, dev, group)
+        return 0
 
     log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")
     t_setup = time.perf_counter()
@@ -406,9 +418,7 @@ def main(argv=None):
     log(f"[bench] B=1 sweep: {step_s * 1e3:.3f} ms/step, {gbs:.1f} GB/s ({gbs / perfmodel.HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     # dominant kernel: the fused gate/up GEMV (55% of the bytes), HIP events on its stream
-    durs = sweep.time_kernel("gate_proj+up_proj")
-    d_avg = float(np.mean([d for d, _ in durs]))
-    qw0 = durs[0][1]
+    d_avg, qw0, n_timed = sweep.time_kernel("gate_proj+up_proj")
     kbytes = perfmodel.gemm_read_bytes(1, qw0.out_features, qw0.in_features, group)
     k_gbs = kbytes / d_avg / 1e9
     log(f"[bench] gate/up GEMV {qw0.out_features}x{qw0.in_features}: {d_avg * 1e6:.2f} us, {k_gbs:.1f} GB/s")
@@ -417,7 +427,7 @@ def main(argv=None):
                 "frac": round(k_gbs / perfmodel.HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "kernel": f"gemv_kernel, fused gate/up {qw0.out_features}x{qw0.in_features}, B=1, g=128",
-                "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes, "launches_timed": len(durs)}
+                "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes, "launches_timed": n_timed}
 
     extras = {}
     if not args.no_extras:
