@@ -17,8 +17,9 @@ Sources, cited by page title and section throughout:
 [ARG]  "Post-training quantization: GPTQ, AWQ and rotation" (arganzheng.life,
        part 03 of the efficient-inference series) -- section 二.2 (quantization
        form, granularity, bits per weight), 二.3 (W4A16 dataflow), 三.1 (step
-       alpha/7 and the Delta^2/12 noise model), 六.2 (the four-weight RTN/AWQ
-       table), 八.2 (41.86 -> scale 5.9805).
+       alpha/7 and the Delta^2/12 noise model), 三.2 (clipping vs rounding, the
+       range search), 六.2 (the four-weight RTN/AWQ table), 八.2 (41.86 -> scale
+       5.9805).
 [WIKI] "压缩算法" (cs-knowledge-wiki.pages.dev) -- section 7.4.1.1 (asymmetric
        s = (max-min)/(2^b-1), z = round(-min/s)), 7.4.1.2 (INT4 group code,
        clamp [-8, 7], two INT4 codes packed into one byte).
@@ -56,3 +57,4 @@ from .layout import (  # noqa: F401
     groupwise_from_device,
 )
 from .gemm import gemm_ref, gemm_ref_rows, to_fp16  # noqa: F401
+from .clip import clip_scale_fp16, clip_codes, clip_errors, quantize_sym_clip  # noqa: F401

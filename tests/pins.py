@@ -424,4 +424,110 @@ def pin_product_special_cases():
     assert np.allclose(o.gemm_ref(2 * x1 - x2, wh), 2 * o.gemm_ref(x1, wh) - o.gemm_ref(x2, wh), rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------- clipping search ([ARG] section 三.2)
+
+
+def _round_half_even(fr: Fraction) -> int:
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def pin_clip_100_is_rtn(seed=21):
+    """With only alpha = 1 to search, the clipping search is RTN bit for bit."""
+    o = _orc()
+    for g in (32, 64, 128, 256):
+        W = synth.weight(32, 1024, seed=seed + g)
+        q, s, p = o.quantize_sym_clip(W, g, 100)
+        q0, s0 = o.quantize_sym(W, g)
+        assert np.array_equal(q, q0) and np.array_equal(s.view(np.uint16), s0.view(np.uint16))
+        assert np.all(p == 100)
+
+
+def pin_clip_scale_rounding(seed=23):
+    """s16_p lies within 2^-10.9 (relative) of the exact p/100 * amax / 7, grows with p,
+    and equals the RTN scale at p = 100."""
+    o = _orc()
+    rng = np.random.default_rng(seed)
+    amax = np.concatenate([rng.uniform(1e-3, 60000, 4000), 7.0 * 2.0 ** np.arange(-14, 13)]).astype(np.float16)
+    prev = None
+    for p in range(1, 101):
+        s = o.clip_scale_fp16(amax, p).astype(np.float64)
+        exact = (p / 100) * amax.astype(np.float64) / 7
+        big = exact > 2 ** -14  # normal float16 range
+        assert np.all(np.abs(s[big] - exact[big]) <= exact[big] * 2 ** -10.9)
+        if prev is not None:
+            assert np.all(s >= prev)
+        prev = s
+    assert np.array_equal(o.clip_scale_fp16(amax, 100).view(np.uint16), o.sym_scale_fp16(amax).view(np.uint16))
+
+
+def pin_clip_exact_bruteforce(seed=22):
+    """Exact rational brute force of the search on small matrices: codes by exact
+    round-half-even of w/s16 clipped to +-7, errors as exact rationals, smallest
+    error with ties to the larger percent."""
+    o = _orc()
+    for g, pmin, N, K in ((32, 85, 6, 96), (64, 90, 3, 128)):
+        W = synth.weight(N, K, seed=seed + g)
+        W[0, :g] = np.float16(0)                              # zero group: every error 0 -> p = 100
+        W[1, :g] = np.float16(7 * 2.0 ** -4) * np.where(np.arange(g) % 2, 1, -1).astype(np.float16)  # exact at p = 100
+        q, s, p = o.quantize_sym_clip(W, g, pmin)
+        Wg = W.reshape(N, -1, g)
+        for n in range(N):
+            for j in range(Wg.shape[1]):
+                w = [Fraction(float(v)) for v in Wg[n, j]]
+                amax = np.abs(Wg[n, j]).max()
+                best = None
+                for pc in range(pmin, 101):
+                    s16 = o.clip_scale_fp16(amax, pc)
+                    sf = Fraction(float(s16))
+                    codes = [0] * g if sf == 0 else [max(-7, min(7, _round_half_even(v / sf))) for v in w]
+                    err = sum((sf * c - v) ** 2 for c, v in zip(codes, w))
+                    if best is None or err <= best[0]:
+                        best = (err, pc, codes, s16)
+                assert int(p[n, j]) == best[1], (n, j, int(p[n, j]), best[1])
+                assert q[n, j * g:(j + 1) * g].tolist() == best[2]
+                assert s[n, j].view(np.uint16) == best[3].view(np.uint16)
+        assert p[0, 0] == 100 and s[0, 0] == 0 and p[1, 0] == 100
+
+
+def pin_clip_never_worse_than_rtn(seed=24):
+    """Per group, the chosen codes reconstruct the weights at least as well as RTN's
+    (alpha = 1 is one of the candidates), codes stay in -7..7, and Gaussian weights
+    at g = 128 lose much of their error (about a fifth)."""
+    o = _orc()
+    W = synth.weight(64, 1024, seed=seed)
+    for g in (32, 128):
+        q, s, p = o.quantize_sym_clip(W, g, 80)
+        assert q.min() >= -7 and q.max() <= 7 and p.min() >= 80 and p.max() <= 100
+        q0, s0 = o.quantize_sym(W, g)
+        e = (o.dequant_sym(q, s, g) - W.astype(np.float64)) ** 2
+        e0 = (o.dequant_sym(q0, s0, g) - W.astype(np.float64)) ** 2
+        eg = e.reshape(64, -1, g).sum(axis=2)
+        e0g = e0.reshape(64, -1, g).sum(axis=2)
+        assert np.all(eg <= e0g)
+        if g == 128:
+            assert eg.sum() < 0.9 * e0g.sum()
+
+
+def pin_clip_gaussian_range():
+    """[ARG] section 三.2: for Gaussian weights the MSE-optimal 4-bit range is about
+    2.5-3 sigma while the maximum sits at 4-5 sigma. Large Gaussian groups searched
+    from 0.4 amax choose a range of 2.3-3.1 sigma (2.48 measured)."""
+    o = _orc()
+    W = synth.weight(32, 8192, seed=3)
+    g = 4096
+    q, s, p = o.quantize_sym_clip(W, g, 40)
+    Wg = W.astype(np.float64).reshape(32, -1, g)
+    sig = Wg.std(axis=2)
+    amax = np.abs(Wg).max(axis=2)
+    chosen = p / 100 * amax / sig
+    assert 3.5 < (amax / sig).mean() < 4.5
+    assert 2.3 < chosen.mean() < 3.1
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

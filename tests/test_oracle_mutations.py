@@ -11,6 +11,7 @@ import oracle
 import oracle.gemm
 import oracle.layout
 import oracle.rtn
+import oracle.clip
 from pins import ALL_PINS
 
 
@@ -155,10 +156,60 @@ def _asym_levels16(monkeypatch):
     monkeypatch.setattr(oracle.rtn, "asym_scale_fp16", lambda mn, mx, levels=15: orig(mn, mx, 16))
 
 
+def _clip_ties_to_smaller(monkeypatch):
+    orig = oracle.clip.clip_errors
+
+    def quant(W16, g, min_percent=80):
+        W = np.asarray(W16)
+        Wg = W.reshape(W.shape[0], -1, g)
+        errs = orig(W, g, min_percent)
+        percent = np.argmin(errs, axis=0) + min_percent        # first (smallest) percent wins ties
+        amax = np.abs(Wg).max(axis=2)
+        s16 = np.zeros(amax.shape, dtype=np.float16)
+        for p in np.unique(percent):
+            s16[percent == p] = oracle.clip.clip_scale_fp16(amax[percent == p], int(p))
+        return oracle.clip.clip_codes(Wg, s16).astype(np.int8).reshape(W.shape), s16, percent
+
+    monkeypatch.setattr(oracle, "quantize_sym_clip", quant)
+
+
+def _clip_qmin8(monkeypatch):
+    def codes(Wg16, s16):
+        s32 = np.asarray(s16, dtype=np.float16).astype(np.float32)[..., None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.clip(np.rint(Wg16.astype(np.float32) / s32), -8, 7)
+        return np.where(s32 == 0, 0.0, q)
+
+    monkeypatch.setattr(oracle.clip, "clip_codes", codes)
+    monkeypatch.setattr(oracle, "clip_codes", codes)
+
+
+def _clip_error_on_codes(monkeypatch):
+    def errs(W16, g, min_percent=80):
+        W = np.asarray(W16)
+        Wg = W.reshape(W.shape[0], -1, g)
+        amax = np.abs(Wg).max(axis=2)
+        out = []
+        for p in range(min_percent, 101):
+            s16 = oracle.clip.clip_scale_fp16(amax, p)
+            q = oracle.clip.clip_codes(Wg, s16)
+            d = q - Wg.astype(np.float64)                      # forgot the scale
+            out.append((d * d).sum(axis=2))
+        return np.stack(out)
+
+    monkeypatch.setattr(oracle.clip, "clip_errors", errs)
+
+
+def _clip_without_100(monkeypatch):
+    orig = oracle.clip.clip_scale_fp16
+    monkeypatch.setattr(oracle.clip, "clip_scale_fp16", lambda a, p: orig(a, min(p, 99)))
+
+
 MUTATIONS = [
     _scale_div8, _scale_two_alpha_over_15, _truncate, _half_away, _fp16_quotient, _nibbles_swapped,
     _device_nibble_order, _device_lane_order, _dequant_wrong_group, _gemm_rows_reversed,
     _gemm_fp16_accumulate, _asym_zero_sign, _asym_dequant_plus, _asym_levels16,
+    _clip_ties_to_smaller, _clip_qmin8, _clip_error_on_codes, _clip_without_100,
 ]
 
 
