@@ -245,7 +245,9 @@ def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
 
 
 def extras_quantize(dev):
-    """Heavy-tailed 14336x4096: quantize+pack throughput and the B = 1 GEMV, g in {32, 64, 128}."""
+    """Heavy-tailed 14336x4096: quantize+pack throughput and the B = 1 GEMV, g in {32, 64, 128};
+    the clipping search's time and weight error against RTN."""
+    import numpy as np
     import torch
 
     import synth
@@ -280,6 +282,32 @@ def extras_quantize(dev):
                 "quantize_us": round(tq * 1e6, 2), "quantize_GBps": round(qb / tq / 1e9, 1),
                 "gemv_us": round(tg * 1e6, 2), "gemv_GBps": round(gb / tg / 1e9, 1)}
             del qws
+        # clipping search (alpha = 0.80 .. 1.00 of the group amax): time, and the weight
+        # reconstruction error against RTN's (dequantized from the library's own codes)
+        torch.cuda.synchronize()
+        a, b = events()
+        a.record()
+        for W in Ws[:4]:
+            qc = q4.quantize_pack_clip(W, g, 80)
+        b.record()
+        torch.cuda.synchronize()
+        tc = a.elapsed_time(b) / 1e3 / 4
+        qr = q4.quantize_pack(base, g)
+        mse = {}
+        for name, qw in (("rtn", qr), ("clip", qc)):
+            codes, scales, _ = q4.to_canonical(qw)
+            c = codes.cpu().numpy()
+            lo = (c & 0xF).astype(np.int8)
+            hi = (c >> 4).astype(np.int8)
+            q = np.empty((N, K), dtype=np.int8)
+            q[:, 0::2] = np.where(lo > 7, lo - 16, lo)
+            q[:, 1::2] = np.where(hi > 7, hi - 16, hi)
+            w_hat = q.astype(np.float32) * np.repeat(scales.cpu().numpy().astype(np.float32), g, axis=1)
+            mse[name] = float(np.mean((w_hat - Wh.astype(np.float32)) ** 2))
+        out[f"g{g}_sym_clip80"] = {"quantize_us": round(tc * 1e6, 2),
+                                   "quantize_GBps": round(perfmodel.quantize_bytes(N, K, g, False) / tc / 1e9, 1),
+                                   "weight_mse": mse["clip"], "weight_mse_rtn": mse["rtn"],
+                                   "mse_ratio": round(mse["clip"] / mse["rtn"], 4)}
     return out
 
 

@@ -114,6 +114,19 @@ q4_status q4_quantize_pack(const void* W, int64_t out, int64_t in, int32_t group
 q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t group,
                                 void* packed, void* scales, void* zeros, void* stream);
 
+/* Symmetric INT4 quantize + pack with the clipping search of [ARG] section 三.2:
+ * per group, for p = min_percent .. 100 (alpha = float32(p) / 100.0f):
+ *   s16_p = float16_rne(float32(max(float32(amax) * alpha, 1e-12f)) / 7.0f)
+ *   q_p   = clamp(rint(w / s16_p), -7, 7)   (0 where s16_p == 0)
+ *   err_p = sum over the group of (s16_p * q_p - w)^2   (float64 accumulation
+ *           of float32-exact differences)
+ * and the p with the smallest err_p is kept, equal errors going to the larger p;
+ * min_percent = 100 gives exactly q4_quantize_pack's output. Output layout and
+ * alignment as q4_quantize_pack (the GEMM reads it unchanged). group must be 32,
+ * 64 or 128 and min_percent in 1..100, else Q4_ERR_UNSUPPORTED. */
+q4_status q4_quantize_pack_clip(const void* W, int64_t out, int64_t in, int32_t group, int32_t min_percent,
+                                void* packed, void* scales, void* stream);
+
 /* Bytes of device workspace q4_gemm / q4_gemm_asym need for this shape: float32
  * partial sums when the channel range is split over several workgroups (a long
  * `in` with B <= 16, or too few rows to fill the GPU); 0 when none is needed. The

@@ -81,6 +81,13 @@ def test_quantize_validation(lib):
     assert f(FAKE, 16, 128, 128, FAKE + 8, FAKE, None) == 4      # packed misaligned
     assert f(FAKE, 16, 128, 128, FAKE, FAKE + 2, None) == 4      # scales misaligned
     assert lib.q4_quantize_pack_asym(FAKE, 16, 128, 128, FAKE, FAKE, None, None) == 1
+    c = lib.q4_quantize_pack_clip
+    assert c(FAKE, 16, 128, 128, 0, FAKE, FAKE, None) == 5                # min_percent below 1
+    assert c(FAKE, 16, 128, 128, 101, FAKE, FAKE, None) == 5              # min_percent above 100
+    assert c(FAKE, 16, 512, 256, 80, FAKE, FAKE, None) == 5               # group outside 32/64/128
+    assert c(None, 16, 128, 128, 80, FAKE, FAKE, None) == 1
+    assert c(FAKE, 16, 96, 64, 80, FAKE, FAKE, None) == 3                 # in % group != 0
+    assert c(FAKE + 2, 16, 128, 128, 80, FAKE, FAKE, None) == 4
 
 
 def test_gemm_validation(lib):

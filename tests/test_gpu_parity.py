@@ -91,6 +91,69 @@ def test_quantize_heavy_tailed_full(q4, g, asym):
     _check_quant_exact(q4, W, g, asym, device_layout=False)
 
 
+def _check_clip_exact(q4, W, g, pmin, rows=None):
+    """q4_quantize_pack_clip against the oracle's clipping search: canonical codes and
+    scales bit for bit (on `rows` only when given: rows are quantized independently)."""
+    qw = q4.quantize_pack_clip(to_gpu(W), g, pmin)
+    codes, scales, _ = q4.to_canonical(qw)
+    Wo = W if rows is None else W[rows]
+    q_o, s_o, _ = oracle.quantize_sym_clip(Wo, g, pmin)
+    c = to_np(codes) if rows is None else to_np(codes)[rows]
+    sc = to_np(scales) if rows is None else to_np(scales)[rows]
+    assert np.array_equal(c, oracle.pack_canonical(q_o)), (W.shape, g, pmin, "codes")
+    assert np.array_equal(sc.view(np.uint16), s_o.view(np.uint16)), (W.shape, g, pmin, "scales")
+    return qw, q_o, s_o
+
+
+@pytest.mark.parametrize("pmin", [80, 100, 1])
+@pytest.mark.parametrize("N,K,g", [(17, 96, 32), (33, 192, 64), (40, 352, 32), (48, 384, 128), (129, 640, 64),
+                                   (100, 1280, 128)])
+def test_quantize_clip_bit_exact(q4, N, K, g, pmin):
+    say(f"quantize clip N={N} K={K} g={g} pmin={pmin}")
+    W = synth.weight(N, K, seed=N * 3 + K)
+    qw, q_o, s_o = _check_clip_exact(q4, W, g, pmin)
+    assert np.array_equal(to_np(qw.packed), oracle.codes_to_device(q_o, symmetric=True)), "device codes"
+    if pmin == 100:
+        q_r, s_r = oracle.quantize_sym(W, g)
+        assert np.array_equal(q_o, q_r) and np.array_equal(s_o.view(np.uint16), s_r.view(np.uint16))
+
+
+def test_quantize_clip_edge_values(q4):
+    N, K = 37, 384
+    cases = {
+        "ties_and_zero_groups": synth.uniform_codes_weight(N, K, seed=1),
+        "all_zero": np.zeros((N, K), dtype=np.float16),
+        "tiny": (synth.weight(N, K, seed=2).astype(np.float32) * np.float32(1e-4)).astype(np.float16),
+        "huge": (synth.weight(N, K, seed=3).astype(np.float32) * np.float32(2.0e4)).clip(-65504, 65504).astype(np.float16),
+        "constant_rows": np.full((N, K), 0.5, dtype=np.float16),
+        "heavy_tailed": synth.heavy_tailed_weight(N, K, seed=6)[0],
+    }
+    for name, W in cases.items():
+        for g in (32, 128):
+            say(f"  clip {name} g={g}")
+            _check_clip_exact(q4, W, g, 80)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_quantize_clip_heavy_tailed_full(q4, g):
+    """The heavy-tailed 14336x4096 workload with the clipping search (alpha 0.80..1.00),
+    checked bit for bit on 512 sampled rows (rows are quantized independently)."""
+    say(f"quantize clip heavy-tailed 14336x4096 g={g}")
+    W, _ = synth.heavy_tailed_weight(14336, 4096, seed=5)
+    rows = np.sort(np.random.default_rng(g).choice(14336, 512, replace=False))
+    _check_clip_exact(q4, W, g, 80, rows=rows)
+
+
+def test_gemm_on_clip_weights(q4):
+    """The product reads clip-searched codes (-7..7) like RTN ones."""
+    for B, N, K, g in ((1, 300, 2048, 128), (4, 129, 640, 64), (40, 100, 1280, 32)):
+        say(f"  gemm on clip weights B={B} N={N} K={K} g={g}")
+        W = synth.weight(N, K, seed=B + N)
+        x = synth.activation(B, K, seed=K)
+        qw, q_o, s_o = _check_clip_exact(q4, W, g, 80)
+        assert_close(to_np(q4.gemm(to_gpu(x), qw)), _ref_product(x, q_o, s_o, None, g), f"clip B={B}")
+
+
 def test_quantize_single_layer_full(q4):
     """4096x4096, N(0, 0.02^2), g=128, seed 0: codes and scales bit-exact, layout included."""
     say("quantize 4096x4096 g=128")

@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     groups_count,
     packed_bytes,
     quantize_pack,
+    quantize_pack_clip,
     status_str,
     to_canonical,
     version,
@@ -23,6 +24,6 @@ from .ops import (  # noqa: F401
 )
 
 __all__ = [
-    "Q4Error", "QuantizedWeight", "quantize_pack", "gemm", "gemm_config", "to_canonical",
+    "Q4Error", "QuantizedWeight", "quantize_pack", "quantize_pack_clip", "gemm", "gemm_config", "to_canonical",
     "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "status_str", "version",
 ]

@@ -228,25 +228,33 @@ size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group) {
 }
 
 static q4_status quantize_common(const void* W, int64_t out, int64_t in, int32_t group, void* packed, void* scales,
-                                 void* zeros, bool asym, void* stream) {
+                                 void* zeros, bool asym, int clip_pmin, void* stream) {
   if (!W || !packed || !scales || (asym && !zeros)) return fail(Q4_ERR_NULL, "W, packed, scales%s must be non-NULL", asym ? ", zeros" : "");
   Dims d;
   q4_status st = check_dims(out, in, group, &d);
   if (st != Q4_OK) return st;
   if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 8))
     return fail(Q4_ERR_ALIGN, "W and packed need 16-byte, scales 8-byte alignment");
-  q4::QuantArgs a{W, d.N, d.K, d.group, d.Np, d.Kp, d.Gp, asym, packed, scales, zeros};
+  q4::QuantArgs a{W, d.N, d.K, d.group, d.Np, d.Kp, d.Gp, asym, packed, scales, zeros, clip_pmin};
   return hip_status(q4::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
 q4_status q4_quantize_pack(const void* W, int64_t out, int64_t in, int32_t group, void* packed, void* scales,
                            void* stream) {
-  return quantize_common(W, out, in, group, packed, scales, nullptr, false, stream);
+  return quantize_common(W, out, in, group, packed, scales, nullptr, false, 0, stream);
 }
 
 q4_status q4_quantize_pack_asym(const void* W, int64_t out, int64_t in, int32_t group, void* packed, void* scales,
                                 void* zeros, void* stream) {
-  return quantize_common(W, out, in, group, packed, scales, zeros, true, stream);
+  return quantize_common(W, out, in, group, packed, scales, zeros, true, 0, stream);
+}
+
+q4_status q4_quantize_pack_clip(const void* W, int64_t out, int64_t in, int32_t group, int32_t min_percent,
+                                void* packed, void* scales, void* stream) {
+  if (min_percent < 1 || min_percent > 100) return fail(Q4_ERR_UNSUPPORTED, "min_percent=%d not in 1..100", (int)min_percent);
+  if (group != 32 && group != 64 && group != 128)
+    return fail(Q4_ERR_UNSUPPORTED, "the clipping search runs for group 32, 64 or 128 (got %d)", (int)group);
+  return quantize_common(W, out, in, group, packed, scales, nullptr, false, min_percent, stream);
 }
 
 static q4_status gemm_common(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,

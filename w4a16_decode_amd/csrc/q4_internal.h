@@ -15,6 +15,7 @@ struct QuantArgs {
   void* packed;
   void* scales;
   void* zeros;
+  int clip_pmin;  // > 0: symmetric clipping search over alpha = p/100, p = clip_pmin..100
 };
 
 struct LayoutArgs {

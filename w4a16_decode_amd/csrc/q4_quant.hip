@@ -142,6 +142,86 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
   }
 }
 
+// Symmetric INT4 with the clipping search of "Post-training quantization: GPTQ, AWQ
+// and rotation" (arganzheng.life), section 三.2: per group, the ranges
+// alpha * amax for alpha = p / 100, p = pmin .. 100, are tried; each gives the RTN
+// scale of that range and codes clipped to the symmetric grid -7 .. 7, and the range
+// whose codes reconstruct the group with the smallest squared error is kept (equal
+// errors go to the larger alpha, so pmin = 100 is plain RTN). Same tile mapping as
+// quant_block_kernel. The error of a candidate: every s16 * q - w is exact in
+// float32, its square exact in float64; each lane sums its weights of the group in
+// float64 and the four lanes of a row exchange partial sums (the same pairs on
+// every lane, so the four agree on the choice).
+__device__ __forceinline__ double wave_sum4(double a) {
+  a += __shfl_xor(a, 16, 64);
+  a += __shfl_xor(a, 32, 64);
+  return a;
+}
+
+__device__ __forceinline__ float clip_q(float w, float s) {
+  return s == 0.0f ? 0.0f : fminf(fmaxf(rintf(w / s), -7.0f), 7.0f);
+}
+
+template <int GSUB>
+__global__ __launch_bounds__(256) void quant_clip_kernel(const uint16_t* __restrict__ W, int N, int K, int S, int Gp,
+                                                         int64_t units, int pmin, uint4* __restrict__ packed,
+                                                         uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  constexpr int MPG = 4 / GSUB;
+
+  for (int64_t u = wave; u < units; u += nwaves) {
+    const int t = (int)(u / S), s = (int)(u % S);
+    const int n = t * kTileRows + r;
+    Row8 w[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+
+    uint32_t dw[4];
+#pragma unroll
+    for (int gs = 0; gs < GSUB; ++gs) {
+      float a = 0.0f;
+#pragma unroll
+      for (int m = gs * MPG; m < (gs + 1) * MPG; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(w[m].v[e]));
+      a = wave_max4(a);
+      double best_err = INFINITY;
+      _Float16 s16 = (_Float16)0.0f;
+      for (int p = pmin; p <= 100; ++p) {
+        const float alpha = (float)p / 100.0f;
+        const _Float16 sp = (_Float16)(fmaxf(a * alpha, 1e-12f) / 7.0f);
+        const float sf = (float)sp;
+        double err = 0.0;
+#pragma unroll
+        for (int m = gs * MPG; m < (gs + 1) * MPG; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double d = (double)(sf * clip_q(w[m].v[e], sf) - w[m].v[e]);
+            err = __builtin_fma(d, d, err);
+          }
+        err = wave_sum4(err);
+        if (err <= best_err) {  // ascending p: ties go to the larger alpha
+          best_err = err;
+          s16 = sp;
+        }
+      }
+      const float scale_f = (float)s16;
+#pragma unroll
+      for (int m = gs * MPG; m < (gs + 1) * MPG; ++m) {
+        uint32_t nib[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nib[e] = (uint32_t)((int)clip_q(w[m].v[e], scale_f) + 8);
+        dw[m] = pack_dword(nib);
+      }
+      if (c == 0) scales[((size_t)t * Gp + (size_t)s * GSUB + gs) * kTileRows + r] = half_bits(s16);
+    }
+    packed[((size_t)t * S + s) * kWave + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+}
+
 // Groups of g = 128*J channels, J >= 2: one wavefront per (tile, group); the
 // group's blocks are read twice (reduction pass, then coding pass).
 template <bool ASYM>
@@ -292,6 +372,17 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   uint4* P = static_cast<uint4*>(a.packed);
   uint16_t* Sc = static_cast<uint16_t*>(a.scales);
   uint8_t* Z = static_cast<uint8_t*>(a.zeros);
+  if (a.clip_pmin > 0) {  // symmetric, g <= 128 (checked by the caller)
+    const int64_t units = (int64_t)T * S;
+    const int grid = grid_for(units * kWave, block);
+    if (a.group == 32)
+      hipLaunchKernelGGL((quant_clip_kernel<4>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, a.clip_pmin, P, Sc);
+    else if (a.group == 64)
+      hipLaunchKernelGGL((quant_clip_kernel<2>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, a.clip_pmin, P, Sc);
+    else
+      hipLaunchKernelGGL((quant_clip_kernel<1>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, a.clip_pmin, P, Sc);
+    return hipGetLastError();
+  }
   if (a.group <= kSuperK) {
     const int64_t units = (int64_t)T * S;
     const int grid = grid_for(units * kWave, block);

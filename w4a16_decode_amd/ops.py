@@ -124,6 +124,22 @@ def quantize_pack(W, group: int = 128, asym: bool = False) -> QuantizedWeight:
     return qw
 
 
+def quantize_pack_clip(W, group: int = 128, min_percent: int = 80) -> QuantizedWeight:
+    """q4_quantize_pack_clip: symmetric INT4 with the per-group clipping search
+    (alpha = p/100, p = min_percent..100); same packed format as quantize_pack."""
+    import torch
+
+    _require_gpu(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [out_features, in_features]")
+    out_features, in_features = W.shape
+    qw = _alloc_qw(out_features, in_features, group, False, W.device)
+    st = _lib.load().q4_quantize_pack_clip(W.data_ptr(), out_features, in_features, group, min_percent,
+                                           qw.packed.data_ptr(), qw.scales.data_ptr(), _stream(W))
+    _check(st)
+    return qw
+
+
 def _prep_gemm(x, qw: QuantizedWeight, out):
     import torch
 
