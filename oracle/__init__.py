@@ -58,3 +58,14 @@ from .layout import (  # noqa: F401
 )
 from .gemm import gemm_ref, gemm_ref_rows, to_fp16  # noqa: F401
 from .clip import clip_scale_fp16, clip_codes, clip_errors, quantize_sym_clip  # noqa: F401
+from .w8 import (  # noqa: F401
+    w8_scale_fp16,
+    w8_codes,
+    quantize_w8,
+    dequant_w8,
+    gemm_w8_rows,
+    w8_device_shapes,
+    w8_codes_to_device,
+    w8_codes_from_device,
+    w8_scales_to_device,
+)

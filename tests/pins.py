@@ -530,4 +530,171 @@ def pin_clip_gaussian_range():
     assert 2.3 < chosen.mean() < 3.1
 
 
+# ------------------------------------- per-channel INT8 RTN (W8A16, oracle/w8.py)
+
+
+def pin_w8_outlier_example():
+    """[ARG] section 七.1: a vector holding one 1000 among ones has the INT8 step
+    1000/127 (about 8), and every other element quantizes to zero."""
+    o = _orc()
+    W = np.ones((1, 64), dtype=np.float16)
+    W[0, 5] = np.float16(1000)
+    q, s = o.quantize_w8(W)
+    assert abs(float(s[0]) - 1000 / 127) <= (1000 / 127) * 2 ** -11 and 7.8 < float(s[0]) < 8.0
+    assert q[0, 5] == 127 and np.count_nonzero(q) == 1
+    assert o.dequant_w8(q, s)[0, 5] == 127 * float(s[0])
+
+
+def pin_w8_clipping_example():
+    """[IOC] section 1.2: W = 1000 against the INT8 range [-127, 127] at scale 1
+    saturates at 127, a clipping error of 873."""
+    o = _orc()
+    W = np.array([[1000.0, -1000.0, 126.0]], dtype=np.float16)
+    q = o.w8_codes(W, np.array([1.0], dtype=np.float16))
+    assert q.tolist() == [[127, -127, 126]]
+    assert float(W[0, 0]) - o.dequant_w8(q, np.array([1.0], dtype=np.float16))[0, 0] == 873.0
+
+
+def pin_w8_hand_rows():
+    """Rows whose amax is 127 * 2^k have an exact scale 2^k; codes worked by hand,
+    ties to even: 254 -> 127, 1 -> 0.5 -> 0, -3 -> -1.5 -> -2, 128 -> 64, 5 -> 2.5 -> 2."""
+    o = _orc()
+    W = np.array([[254.0, 1.0, -3.0, 128.0, 5.0],
+                  [0.0, 0.0, 0.0, 0.0, 0.0],
+                  [-0.4960938, 0.25, 0.0058594, -0.0058594, 0.0]], dtype=np.float16)
+    q, s = o.quantize_w8(W)
+    assert s.tolist() == [2.0, 0.0, float(np.float16(0.4960938) / np.float16(127))]
+    assert q[0].tolist() == [127, 0, -2, 64, 2]
+    assert q[1].tolist() == [0, 0, 0, 0, 0]           # W3: zero row -> codes 0, scale 0
+    # row 2: amax = 127 * 2^-8 exactly, s = 2^-8: 0.25 -> 64, +-0.0058594 (1.5 * 2^-8) -> +-2
+    assert float(s[2]) == 2.0 ** -8 and q[2].tolist() == [-127, 64, 2, -2, 0]
+
+
+def pin_w8_scale_exhaustive():
+    """fp16(fp32(a)/127) is the correctly rounded a/127 for every float16 a >= 0, and
+    the quick code example's clamp of amax at 1e-6 changes no float16 scale (W1)."""
+    o = _orc()
+    a = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    s = o.w8_scale_fp16(a)
+    assert np.array_equal(s.view(np.uint16), (a.astype(np.float64) / 127.0).astype(np.float16).view(np.uint16))
+    assert np.array_equal(s.view(np.uint16), o.w8_scale_fp16(a, eps=1e-6).view(np.uint16))
+    for ai, si in zip(a[1::89], s[1::89]):
+        v = Fraction(float(ai)) / 127
+        d = abs(v - Fraction(float(si)))
+        for nb in (np.nextafter(si, np.float16(0)), np.nextafter(si, np.float16(np.inf))):
+            dn = abs(v - Fraction(float(nb)))
+            # a tie goes to the even significand
+            assert d < dn or (d == dn and (si.view(np.uint16) & 1) == 0)
+
+
+def pin_w8_code_decision_exact(n_scales=60, seed=31):
+    """rint of the IEEE float32 quotient equals the exact rational decision for every
+    float16 w with |w| <= amax of a row whose scale is s16 (W2)."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    all16 = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    all16 = np.concatenate([all16, -all16[1:]])
+    tried = 0
+    for b in r.integers(0x0200, 0x5400, size=n_scales).astype(np.uint16):
+        s16 = np.array([b], dtype=np.uint16).view(np.float16)[0]
+        amax = np.float16(127 * float(s16))
+        if not np.isfinite(amax) or o.w8_scale_fp16(np.array([amax]))[0] != s16:
+            continue
+        tried += 1
+        w = all16[np.abs(all16.astype(np.float64)) <= float(amax)]
+        sv = float(s16)
+        q32 = np.clip(np.rint(w.astype(np.float32) / np.float32(sv)), -127, 127)
+        q64 = np.clip(np.rint(w.astype(np.float64) / sv), -127, 127)
+        assert np.array_equal(q32, q64), sv
+        near = np.abs(np.abs(w.astype(np.float64) / sv) % 1.0 - 0.5) < 1e-9
+        for wi, qi in zip(w[near], q64[near]):
+            assert qi == max(-127, min(127, _round_half_even(Fraction(float(wi)) / Fraction(sv))))
+        K = 256
+        n_full = (w.size // (K - 1)) * (K - 1)
+        rows = w[:n_full].reshape(-1, K - 1)
+        Wm = np.concatenate([np.full((rows.shape[0], 1), amax, dtype=np.float16), rows], axis=1)
+        q, s_or = o.quantize_w8(Wm)
+        assert np.all(s_or == s16)
+        assert np.array_equal(q[:, 1:].astype(np.float64).ravel(), q64[:n_full])
+    assert tried >= 20
+
+
+def pin_w8_invariants(seed=32):
+    """[ARG] section 七.5: the INT8 step is absolute, every error within s/2; codes
+    stay in -127..127 (never -128, also under subnormal scales), the row maximum maps
+    to +-127, and the map is odd."""
+    o = _orc()
+    W = synth.weight(64, 2048, seed=seed)
+    W[3] *= np.float16(1e-3)                     # amax ~1e-4: scale near the float16 subnormals
+    W[4] = np.float16(0)
+    W[4, 7] = np.float16(-1e-5)                  # scale a subnormal far below amax/127
+    W[4, 9] = np.float16(9e-6)
+    q, s = o.quantize_w8(W)
+    assert q.min() >= -127 and q.max() <= 127
+    assert q[4, 7] == -127 and q[4, 9] == 127
+    err = np.abs(o.dequant_w8(q, s) - W.astype(np.float64))
+    normal = s.astype(np.float64) >= 2.0 ** -14
+    assert np.all(err[normal] <= s.astype(np.float64)[normal, None] / 2)
+    am = np.abs(W).argmax(axis=1)
+    assert np.all(np.abs(q[np.arange(64), am])[normal] == 127)
+    qn, sn = o.quantize_w8(-W)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+
+
+def pin_w8_noise_model(N=512, K=4096, seed=33):
+    """[ARG] section 三.1: uniform noise Delta^2/12 per weight; the row maximum is
+    reproduced exactly, so the mean over rows of ((K-1)/K) s^2/12 (within 1%)."""
+    o = _orc()
+    W = synth.weight(N, K, seed=seed)
+    q, s = o.quantize_w8(W)
+    mse = o.quant_mse(W, o.dequant_w8(q, s))
+    model = float(np.mean(s.astype(np.float64) ** 2)) / 12 * (K - 1) / K
+    assert abs(mse / model - 1) < 0.01, mse / model
+    # and INT8 per-channel beats INT4 at g = 128 by more than 50x (ARG section 四.3: nearly lossless)
+    q4, s4 = o.quantize_sym(W, 128)
+    assert o.quant_mse(W, o.dequant_sym(q4, s4, 128)) > 50 * mse
+
+
+def pin_w8_layout_hand_positions():
+    """Single codes planted at hand-computed device positions of the W8 layout."""
+    o = _orc()
+    N, K = 40, 352
+    sh = o.w8_device_shapes(N, K)
+    assert (sh["Np"], sh["Kp"], sh["S"], sh["code_bytes"]) == (48, 384, 3, 48 * 384)
+    # (n, k, byte) from the spec, ((t*S + s)*2 + h)*1024 + (r + 16c)*16 + 8m + e:
+    #   n=17,k=200: t=1 r=1 s=1 h=1 m=0 c=1 e=0 -> ((1*3+1)*2+1)*1024 + 17*16 + 0 + 0 = 9488
+    #   n=0,k=1:    e=1 -> 1
+    #   n=15,k=127: t=0 r=15 s=0 h=1 m=1 c=3 e=7 -> 1024 + 63*16 + 8 + 7 = 2047
+    #   n=39,k=350: t=2 r=7 s=2 h=1 m=0 c=3 e=6 -> ((2*3+2)*2+1)*1024 + 55*16 + 0 + 6 = 18294
+    for n, k, byte in ((17, 200, 9488), (0, 1, 1), (15, 127, 2047), (39, 350, 18294)):
+        q = np.zeros((N, K), dtype=np.int64)
+        q[n, k] = -5
+        dev = o.w8_codes_to_device(q)
+        assert dev[byte] == 123, (n, k)
+        assert np.all(np.delete(dev, byte) == 128)
+        assert np.array_equal(o.w8_codes_from_device(dev, N, K), q.astype(np.int8))
+    r = np.random.default_rng(3)
+    for N, K in ((16, 128), (33, 96), (5, 32), (48, 1024)):
+        q = r.integers(-127, 128, size=(N, K))
+        dev = o.w8_codes_to_device(q)
+        assert np.array_equal(o.w8_codes_from_device(dev, N, K), q.astype(np.int8))
+        assert np.array_equal(np.sort(dev[dev != 128]), np.sort((q + 128).ravel()[(q != 0).ravel()]))
+    assert o.w8_scales_to_device(np.array([1, 2, 3], dtype=np.float16), 3).tolist() == [1, 2, 3] + [0] * 13
+
+
+def pin_w8_product_bruteforce(seed=34):
+    """Exact rational y = sum_k x * q * s over the codes (pure Python) against the oracle."""
+    o = _orc()
+    for B, N, K in ((1, 5, 32), (3, 17, 64), (2, 4, 200)):
+        W = synth.weight(N, K, seed=seed + N)
+        x = synth.activation(B, K, seed=seed + K)
+        q, s = o.quantize_w8(W)
+        rows = np.arange(N)[::-1]
+        y = o.gemm_w8_rows(x, q, s, rows)
+        for b in range(B):
+            for i, n in enumerate(rows):
+                ex = sum(Fraction(float(x[b, k])) * Fraction(float(s[n])) * int(q[n, k]) for k in range(K))
+                assert abs(y[b, i] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

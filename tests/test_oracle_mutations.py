@@ -12,6 +12,7 @@ import oracle.gemm
 import oracle.layout
 import oracle.rtn
 import oracle.clip
+import oracle.w8
 from pins import ALL_PINS
 
 
@@ -205,11 +206,81 @@ def _clip_without_100(monkeypatch):
     monkeypatch.setattr(oracle.clip, "clip_scale_fp16", lambda a, p: orig(a, min(p, 99)))
 
 
+def _w8_div128(monkeypatch):
+    def sc(a, eps=None):
+        return (np.asarray(a, dtype=np.float16).astype(np.float32) / np.float32(128)).astype(np.float16)
+
+    monkeypatch.setattr(oracle.w8, "w8_scale_fp16", sc)
+    monkeypatch.setattr(oracle, "w8_scale_fp16", sc)
+
+
+def _w8_clamp_m128(monkeypatch):
+    monkeypatch.setattr(oracle.w8, "np", _NumpyWith(clip=lambda a, lo, hi: np.clip(a, -128 if lo == -127 else lo, hi)))
+
+
+def _w8_truncate(monkeypatch):
+    monkeypatch.setattr(oracle.w8, "np", _NumpyWith(rint=np.trunc))
+
+
+def _w8_half_away(monkeypatch):
+    monkeypatch.setattr(oracle.w8, "np", _NumpyWith(rint=lambda a: np.sign(a) * np.floor(np.abs(a) + 0.5)))
+
+
+def _w8_fp16_quotient(monkeypatch):
+    monkeypatch.setattr(oracle.w8, "np",
+                        _NumpyWith(rint=lambda a: np.rint(np.asarray(a).astype(np.float16).astype(np.float64))))
+
+
+def _w8_scale_per_column(monkeypatch):
+    def quant(W16):
+        W = np.asarray(W16)
+        amax = np.abs(W).max(axis=0)                         # over rows instead of channels
+        s16 = oracle.w8.w8_scale_fp16(amax)
+        s32 = s16.astype(np.float32)[None, :]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(s32 == 0, 0, np.clip(np.rint(W.astype(np.float32) / s32), -127, 127))
+        return q.astype(np.int8), s16[: W.shape[0]] if s16.size >= W.shape[0] else np.resize(s16, W.shape[0])
+
+    monkeypatch.setattr(oracle, "quantize_w8", quant)
+
+
+def _w8_layout_h_m_swapped(monkeypatch):
+    def pos(N, K):
+        sh = oracle.w8.w8_device_shapes(N, K)
+        n = np.arange(sh["Np"])[:, None]
+        k = np.arange(sh["Kp"])[None, :]
+        t, r = n // 16, n % 16
+        s, m = k // 128, (k % 128) // 64                     # 64-channel halves and 32-channel steps swapped
+        h, c, e = (k % 64) // 32, (k % 32) // 8, k % 8
+        return ((t * sh["S"] + s) * 2 + h) * 1024 + (r + 16 * c) * 16 + 8 * m + e, sh
+
+    monkeypatch.setattr(oracle.w8, "_w8_device_position", pos)
+
+
+def _w8_offset127(monkeypatch):
+    orig_to = oracle.w8.w8_codes_to_device
+
+    def to(q):
+        return (orig_to(q).astype(np.int64) - 1).astype(np.uint8)
+
+    monkeypatch.setattr(oracle, "w8_codes_to_device", to)
+
+
+def _w8_dequant_rows_shifted(monkeypatch):
+    def dq(q, s16):
+        return np.asarray(q, dtype=np.float64) * np.roll(np.asarray(s16, dtype=np.float64), 1)[:, None]
+
+    monkeypatch.setattr(oracle.w8, "dequant_w8", dq)
+    monkeypatch.setattr(oracle, "dequant_w8", dq)
+
+
 MUTATIONS = [
     _scale_div8, _scale_two_alpha_over_15, _truncate, _half_away, _fp16_quotient, _nibbles_swapped,
     _device_nibble_order, _device_lane_order, _dequant_wrong_group, _gemm_rows_reversed,
     _gemm_fp16_accumulate, _asym_zero_sign, _asym_dequant_plus, _asym_levels16,
     _clip_ties_to_smaller, _clip_qmin8, _clip_error_on_codes, _clip_without_100,
+    _w8_div128, _w8_clamp_m128, _w8_truncate, _w8_half_away, _w8_fp16_quotient, _w8_scale_per_column,
+    _w8_layout_h_m_swapped, _w8_offset127, _w8_dequant_rows_shifted,
 ]
 
 
