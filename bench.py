@@ -311,6 +311,62 @@ def extras_quantize(dev):
     return out
 
 
+def extras_w8(dev, int4_us_per_layer: float | None):
+    """W8A16 (per-channel INT8) GEMV on the 70B layer's fused matrices at B in {1, 4, 8}:
+    per-launch time and GB/s (copies of each matrix rotate past the 256 MB last-level
+    cache), the layer total against the INT4 layer, and the INT8 quantizer's time."""
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+    from w4a16_decode_amd import perfmodel
+
+    order = {name: i for i, name in enumerate(synth.MATRIX_ORDER)}
+    out = {}
+    per_layer = {}
+    for grp in synth.FUSED_GROUPS:
+        N = sum(synth.LLAMA3_70B[n][0] for n in grp)
+        K = synth.LLAMA3_70B[grp[0]][1]
+        copies = max(2, -(-600_000_000 // (N * K)))
+        qws = []
+        for c in range(copies):
+            parts = [synth.device_weight(*synth.LLAMA3_70B[n], seed=3, layer=c, matrix=order[n], device=dev)
+                     for n in grp]
+            W = parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
+            del parts
+            if c == 0:  # the quantizer's time on this matrix
+                q4.q8_quantize_pack(W)
+                torch.cuda.synchronize()
+                a, b = events()
+                a.record()
+                for _ in range(3):
+                    q4.q8_quantize_pack(W)
+                b.record()
+                torch.cuda.synchronize()
+                tq = a.elapsed_time(b) / 1e3 / 3
+            qws.append(q4.q8_quantize_pack(W))
+            del W
+        kind = KIND_OF["+".join(grp)]
+        res = {"shape": [N, K], "quantize_us": round(tq * 1e6, 2),
+               "quantize_GBps": round((2 * N * K + perfmodel.w8_weight_bytes(N, K)) / tq / 1e9, 1)}
+        for B in (1, 4, 8):
+            x = synth.device_activation(B, K, seed=3, layer=0, matrix=100, device=dev)
+            y = torch.empty((B, N), dtype=torch.float16, device=dev)
+            ws = torch.empty(max(16, q4.q8_workspace_bytes(B, N, K)), dtype=torch.uint8, device=dev)
+            t = graph_time(lambda: [q4.q8_gemm(x, qw, out=y, workspace=ws) for qw in qws], 5) / copies
+            nb = perfmodel.w8_gemm_read_bytes(B, N, K)
+            res[f"B{B}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+            per_layer[B] = per_layer.get(B, 0.0) + t
+        out[kind] = res
+        log(f"[bench] W8A16 {kind} {N}x{K}: {res}")
+        del qws
+        torch.cuda.empty_cache()
+    out["us_per_layer"] = {str(B): round(t * 1e6, 2) for B, t in per_layer.items()}
+    if int4_us_per_layer:
+        out["vs_int4_layer_b1"] = round(per_layer[1] * 1e6 / int4_us_per_layer, 3)
+    return out
+
+
 def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) -> dict:
     """Oracle (numpy) W4A16 product on whole layers of the 70B sweep, until ~target_s of CPU time."""
     import numpy as np
@@ -403,6 +459,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-kernel", choices=["gate_up", "down", "qkv", "o"])
     ap.add_argument("--only-batch", type=int, default=0)
+    ap.add_argument("--only-w8", action="store_true", help="only the W8A16 layer measurement")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -430,6 +487,9 @@ def main(argv=None):
         return 0
     if args.only_batch:
         only_batch(args.only_batch, args.reps, dev, group)
+        return 0
+    if args.only_w8:
+        log(f"[bench] W8A16: {json.dumps(extras_w8(dev, None))}")
         return 0
 
     log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")
@@ -501,6 +561,9 @@ def main(argv=None):
         torch.cuda.empty_cache()
         extras["heavy_tailed_14336x4096"] = extras_quantize(dev)
         log(f"[bench] heavy-tailed: {extras['heavy_tailed_14336x4096']}")
+        torch.cuda.empty_cache()
+        int4_layer = extras.get("us_per_layer_vs_B_70b", {}).get("1", {}).get("us_per_layer")
+        extras["w8a16_70b_layer"] = extras_w8(dev, int4_layer)
         torch.cuda.empty_cache()
 
     cpu = None

@@ -1,4 +1,4 @@
-"""The C ABI library on the CPU: it loads, exports what include/q4.h declares,
+"""The C ABI library on the CPU: it loads, exports what include/*.h declares,
 shares torch's HIP runtime, and rejects bad arguments before any HIP call.
 
 No test here launches a kernel; each invalid call below returns from the
@@ -29,9 +29,9 @@ def test_exports_every_declared_symbol(lib):
     from w4a16_decode_amd import _lib
 
     declared = _lib.header_functions()
-    assert len(declared) >= 14
+    assert len(declared) >= 22 and "q8_gemm" in declared and "q4_gemm" in declared
     for name in declared:
-        assert hasattr(lib, name), f"{name} declared in include/q4.h but not exported"
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
         assert name in _lib.SIGNATURES, f"{name} has no ctypes signature in the binding"
     assert sorted(_lib.SIGNATURES) == declared
 
@@ -159,3 +159,41 @@ def test_time_model_matches_page_numbers():
     assert abs(perfmodel.time_model_s(0, 7.5e9, 1, 3.35e12, 989e12) * 1e6 - 15.2) < 0.1
     t_w4 = 4.0e9 / 3.35e12
     assert abs(t_w4 / (2 * 7.5e9 / 989e12) - 79) < 1.0
+
+
+def test_w8_sizes_and_validation(lib):
+    assert lib.q8_packed_bytes(4096, 4096) == 4096 * 4096
+    assert lib.q8_packed_bytes(17, 96) == 32 * 128
+    assert lib.q8_packed_bytes(16, 100) == 0                     # in % 8 != 0
+    assert lib.q8_packed_bytes(0, 128) == 0
+    assert lib.q8_scales_count(17) == 32 and lib.q8_scales_count(0) == 0
+    q = lib.q8_quantize_pack
+    assert q(None, 16, 128, FAKE, FAKE, None) == 1
+    assert q(FAKE, 16, 100, FAKE, FAKE, None) == 2
+    assert b"multiple of 8" in lib.q4_last_error()
+    assert q(FAKE, 1 << 30, 128, FAKE, FAKE, None) == 2
+    assert q(FAKE + 2, 16, 128, FAKE, FAKE, None) == 4
+    assert q(FAKE, 16, 128, FAKE + 8, FAKE, None) == 4
+    assert q(FAKE, 16, 128, FAKE, FAKE + 1, None) == 4
+    g = lib.q8_gemm
+    assert g(None, 0, None, None, 16, 128, None, None, 0, None) == 0       # B = 0
+    assert g(FAKE, -1, FAKE, FAKE, 16, 128, FAKE, None, 0, None) == 2
+    assert g(None, 1, FAKE, FAKE, 16, 128, FAKE, None, 0, None) == 1
+    assert g(FAKE, 1, FAKE, FAKE, 16, 124, FAKE, None, 0, None) == 2
+    assert g(FAKE + 4, 1, FAKE, FAKE, 16, 128, FAKE, None, 0, None) == 4
+    assert g(FAKE, 1, FAKE, FAKE, 16, 128, FAKE + 1, None, 0, None) == 4
+    c = lib.q8_gemm_config
+    assert c(FAKE, 1, FAKE, FAKE, 16, 128, FAKE, 3, 1, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, 16, 128, FAKE, 1, 17, 1, None, 0, None) == 5
+    assert c(FAKE, 1, FAKE, FAKE, 16, 256, FAKE, 1, 8, 3, None, 0, None) == 5    # k_splits > blocks
+    assert c(FAKE, 16, FAKE, FAKE, 16, 8192, FAKE, 1, 8, 1, None, 0, None) == 5  # x slice > LDS
+    assert c(FAKE, 1, FAKE, FAKE, 16, 256, FAKE, 1, 1, 2, None, 0, None) == 6    # split needs workspace
+    assert c(FAKE, 1, FAKE, FAKE, 16, 256, FAKE, 1, 1, 2, FAKE + 4, 128, None) == 4
+    # workspace: B = 8 over 28672 channels splits; B > 16 sizes for 16-row slices
+    ws = lib.q8_workspace_bytes(8, 8192, 28672)
+    assert ws > 0 and ws % (8 * 8192 * 4) == 0
+    assert lib.q8_workspace_bytes(1, 4096, 4096) == 0
+    assert lib.q8_workspace_bytes(40, 8192, 28672) == lib.q8_workspace_bytes(16, 8192, 28672)
+    assert lib.q8_gemm(FAKE, 8, FAKE, FAKE, 8192, 28672, FAKE, None, 0, None) == 6
+    assert lib.q8_to_canonical(None, FAKE, 16, 128, FAKE, FAKE, None) == 1
+    assert lib.q8_from_canonical(FAKE, FAKE, 16, 100, FAKE, FAKE, None) == 2

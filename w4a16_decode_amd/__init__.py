@@ -1,8 +1,9 @@
 """w4a16_decode_amd: INT4 group-wise RTN weight quantization and the fused
-W4A16 GEMV / skinny GEMM for AMD MI355X (gfx950).
+W4A16 GEMV / skinny GEMM for AMD MI355X (gfx950), plus per-channel INT8
+weights with the W8A16 GEMV.
 
 Every computation runs in the HIP kernels of ``libq4.so`` behind the C ABI
-declared in ``include/q4.h``; this package only marshals torch tensors
+declared in ``include/q4.h`` and ``include/q8.h``; this package only marshals torch tensors
 (device memory, the current HIP stream) into those calls. There is no CPU
 fallback: without the built library or a GPU the calls raise.
 """
@@ -10,11 +11,19 @@ fallback: without the built library or a GPU the calls raise.
 from .ops import (  # noqa: F401
     Q4Error,
     QuantizedWeight,
+    QuantizedWeight8,
     from_canonical,
     gemm,
     gemm_config,
     groups_count,
     packed_bytes,
+    q8_from_canonical,
+    q8_gemm,
+    q8_gemm_config,
+    q8_packed_bytes,
+    q8_quantize_pack,
+    q8_to_canonical,
+    q8_workspace_bytes,
     quantize_pack,
     quantize_pack_clip,
     status_str,
@@ -26,4 +35,6 @@ from .ops import (  # noqa: F401
 __all__ = [
     "Q4Error", "QuantizedWeight", "quantize_pack", "quantize_pack_clip", "gemm", "gemm_config", "to_canonical",
     "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "status_str", "version",
+    "QuantizedWeight8", "q8_quantize_pack", "q8_gemm", "q8_gemm_config", "q8_to_canonical", "q8_from_canonical",
+    "q8_packed_bytes", "q8_workspace_bytes",
 ]

@@ -14,14 +14,15 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libq4.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "q4.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADERS = (os.path.join(INCLUDE, "q4.h"), os.path.join(INCLUDE, "q8.h"))
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 
-# name -> (restype, argtypes); mirrors include/q4.h
+# name -> (restype, argtypes); mirrors include/q4.h and include/q8.h
 SIGNATURES = {
     "q4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_error": (ctypes.c_char_p, []),
@@ -39,16 +40,27 @@ SIGNATURES = {
                                       _P]),
     "q4_to_canonical": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I32, _P, _P, _P, _P]),
     "q4_from_canonical": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I32, _P, _P, _P, _P]),
+    "q8_packed_bytes": (_SZ, [_I64, _I64]),
+    "q8_scales_count": (_SZ, [_I64]),
+    "q8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "q8_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "q8_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "q8_gemm_config": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I64, _P, _I32, _I32, _I32, _P, _SZ, _P]),
+    "q8_to_canonical": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "q8_from_canonical": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
 }
 
 _lib = None
 
 
-def header_functions(path: str = HEADER) -> list[str]:
-    """Names of the functions include/q4.h declares."""
-    src = open(path, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", src)))
+def header_functions(paths=HEADERS) -> list[str]:
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for path in paths:
+        src = open(path, encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(q[48]_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def load() -> ctypes.CDLL:

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/q4.h"
+#include "../../include/q8.h"
 #include "q4_internal.h"
 
 namespace {
@@ -102,11 +103,11 @@ size_t gemv_lds(int B, int S, int KS, int R, int group, bool asym) {
 }
 
 // Wavefronts a GEMV workgroup runs with (gemv_max_waves in q4_gemm.hip).
-int gemv_max_waves(int R, int group) { return (group < 128 || R > 2) ? 8 : 16; }
+int gemv_max_waves(int R, int group, bool q8 = false) { return (group < 128 || R > 2 || (q8 && R > 1)) ? 8 : 16; }
 
-bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, size_t lds_limit) {
+bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, size_t lds_limit, bool q8 = false) {
   if (KS < 1 || KS > S || W < 1 || W > 16) return false;
-  W = std::min(W, gemv_max_waves(R, group));
+  W = std::min(W, gemv_max_waves(R, group, q8));
   const int nsb = (S + KS - 1) / KS;
   if (gemv_lds(B, S, KS, R, group, asym) > lds_limit) return false;
   return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
@@ -144,12 +145,13 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     // extra tile per load keeps more bytes in flight where there are few row
     // blocks), else one: tall matrices, small groups (several scales per block) and
     // matrices so small that two tiles per row block would leave CUs idle
-    const int R = (T >= 2048 || d.group < 128 || T > S * 8 || T < 512) ? 1 : 2;
+    // (INT8 codes: always one; a 2 KiB block per tile already keeps 8 KiB in flight)
+    const int R = (a->q8 || T >= 2048 || d.group < 128 || T > S * 8 || T < 512) ? 1 : 2;
     // 8 wavefronts (two workgroups per CU) stream best for B <= 4; 16 hold twice
     // the activation slice, which keeps larger batches from splitting the channels
-    const int W = B <= 4 ? 8 : gemv_max_waves(R, d.group);
+    const int W = B <= 4 ? 8 : gemv_max_waves(R, d.group, a->q8);
     int KS = 1;
-    while (KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim)) ++KS;
+    while (KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
     a->rows_per_wave = R;
     a->waves_per_group = W;
     a->k_splits = KS;
@@ -372,6 +374,154 @@ q4_status q4_from_canonical(const void* canon_codes, const void* canon_scales, c
   q4::LayoutArgs a{d.N, d.K, d.group, d.Np, d.Kp, d.Gp, asym != 0, packed, scales, zeros,
                    const_cast<void*>(canon_codes), const_cast<void*>(canon_scales), const_cast<void*>(canon_zeros)};
   return hip_status(q4::launch_from_canonical(a, static_cast<hipStream_t>(stream)), "from_canonical launch");
+}
+
+// ---- per-channel INT8 (W8A16) ------------------------------------------------
+
+static q4_status check_w8_dims(int64_t out, int64_t in, Dims* d) {
+  if (out <= 0 || in <= 0 || out >= kMaxDim || in >= kMaxDim)
+    return fail(Q4_ERR_SHAPE, "out=%lld, in=%lld: each must be in [1, 2^30)", (long long)out, (long long)in);
+  if (in % 8 != 0) return fail(Q4_ERR_SHAPE, "in=%lld must be a multiple of 8", (long long)in);
+  d->N = (int)out;
+  d->K = (int)in;
+  d->Np = (int)round_up(out, 16);
+  d->Kp = (int)round_up(in, 128);
+  d->group = d->Kp;  // one scale per row: a single group spanning the padded row
+  d->Gp = 1;
+  return Q4_OK;
+}
+
+size_t q8_packed_bytes(int64_t out, int64_t in) {
+  Dims d;
+  if (out <= 0 || in <= 0 || out >= kMaxDim || in >= kMaxDim || in % 8 != 0) return 0;
+  check_w8_dims(out, in, &d);
+  return (size_t)d.Np * (size_t)d.Kp;
+}
+
+size_t q8_scales_count(int64_t out) {
+  if (out <= 0 || out >= kMaxDim) return 0;
+  return (size_t)round_up(out, 16);
+}
+
+q4_status q8_quantize_pack(const void* W, int64_t out, int64_t in, void* packed, void* scales, void* stream) {
+  if (!W || !packed || !scales) return fail(Q4_ERR_NULL, "W, packed, scales must be non-NULL");
+  Dims d;
+  q4_status st = check_w8_dims(out, in, &d);
+  if (st != Q4_OK) return st;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2))
+    return fail(Q4_ERR_ALIGN, "W and packed need 16-byte, scales 2-byte alignment");
+  q4::W8Args a{W, d.N, d.K, d.Np, d.Kp, packed, scales, nullptr, nullptr};
+  return hip_status(q4::launch_quantize_w8(a, static_cast<hipStream_t>(stream)), "q8 quantize launch");
+}
+
+size_t q8_workspace_bytes(int64_t B, int64_t out, int64_t in) {
+  Dims d;
+  if (B <= 0 || B >= kMaxDim || out <= 0 || in <= 0 || out >= kMaxDim || in >= kMaxDim || in % 8 != 0) return 0;
+  check_w8_dims(out, in, &d);
+  q4::GemmArgs a{};
+  a.B = (int)std::min<int64_t>(B, 16);
+  a.N = d.N;
+  a.q8 = true;
+  pick_shape(a.B, d, &a);
+  return splits_workspace(a);
+}
+
+static q4_status q8_gemm_common(const void* x, int64_t B, const void* packed, const void* scales, int64_t out,
+                                int64_t in, void* y, int rows_per_wave, int waves_per_group, int k_splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || B >= kMaxDim) return fail(Q4_ERR_SHAPE, "B=%lld out of range", (long long)B);
+  Dims d;
+  q4_status st = check_w8_dims(out, in, &d);
+  if (st != Q4_OK) return st;
+  if (B == 0) return ok();
+  if (!x || !packed || !scales || !y) return fail(Q4_ERR_NULL, "x, packed, scales, y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(y, 2))
+    return fail(Q4_ERR_ALIGN, "x and packed need 16-byte, scales and y 2-byte alignment");
+  if ((int64_t)B * in >= (int64_t(1) << 40) || (int64_t)B * out >= (int64_t(1) << 40))
+    return fail(Q4_ERR_SHAPE, "B*in or B*out too large");
+  const int B16 = (int)std::min<int64_t>(B, 16);
+  q4::GemmArgs a{};
+  a.packed = packed;
+  a.scales = scales;
+  a.q8 = true;
+  a.N = d.N;
+  a.K = d.K;
+  a.group = d.group;
+  a.Np = d.Np;
+  a.Kp = d.Kp;
+  a.Gp = d.Gp;
+  pick_shape(B16, d, &a);
+  if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0) {
+    if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
+      return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave must be 1, 2 or 4");
+    if (waves_per_group < 1 || waves_per_group > 16)
+      return fail(Q4_ERR_UNSUPPORTED, "waves_per_group must be in [1, 16]");
+    a.lds_limit = lds_per_block();
+    if (!gemv_shape_ok(B16, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, false, a.lds_limit, true))
+      return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: more splits than 128-channel blocks, "
+                  "or the activation slice of %d rows does not fit LDS or the copy",
+                  (int)k_splits, (int)waves_per_group, B16);
+    a.rows_per_wave = rows_per_wave;
+    a.waves_per_group = waves_per_group;
+    a.k_splits = k_splits;
+  }
+  a.B = B16;
+  const size_t need = splits_workspace(a);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(Q4_ERR_WORKSPACE, "this shape needs %zu bytes of workspace (q8_workspace_bytes), got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(Q4_ERR_ALIGN, "workspace needs 16-byte alignment");
+  }
+  a.workspace = workspace;
+  // slices of 16 batch rows, in order on the stream (they share the workspace)
+  for (int64_t b0 = 0; b0 < B; b0 += 16) {
+    a.B = (int)std::min<int64_t>(16, B - b0);
+    a.x = static_cast<const uint16_t*>(x) + b0 * in;
+    a.y = static_cast<uint16_t*>(y) + b0 * out;
+    const q4_status s2 = hip_status(q4::launch_gemm(a, static_cast<hipStream_t>(stream)), "q8 gemm launch");
+    if (s2 != Q4_OK) return s2;
+  }
+  return ok();
+}
+
+q4_status q8_gemm(const void* x, int64_t B, const void* packed, const void* scales, int64_t out, int64_t in,
+                  void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return q8_gemm_common(x, B, packed, scales, out, in, y, 0, 0, 0, workspace, workspace_bytes, stream);
+}
+
+q4_status q8_gemm_config(const void* x, int64_t B, const void* packed, const void* scales, int64_t out,
+                         int64_t in, void* y, int32_t rows_per_wave, int32_t waves_per_group, int32_t k_splits,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows_per_wave <= 0 || waves_per_group <= 0 || k_splits <= 0)
+    return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave, waves_per_group and k_splits must be positive");
+  return q8_gemm_common(x, B, packed, scales, out, in, y, rows_per_wave, waves_per_group, k_splits, workspace,
+                        workspace_bytes, stream);
+}
+
+q4_status q8_to_canonical(const void* packed, const void* scales, int64_t out, int64_t in, void* canon_codes,
+                          void* canon_scales, void* stream) {
+  if (!packed || !scales || !canon_codes || !canon_scales) return fail(Q4_ERR_NULL, "a required pointer is NULL");
+  Dims d;
+  q4_status st = check_w8_dims(out, in, &d);
+  if (st != Q4_OK) return st;
+  if (!aligned(scales, 2) || !aligned(canon_scales, 2)) return fail(Q4_ERR_ALIGN, "scales need 2-byte alignment");
+  q4::W8Args a{nullptr, d.N, d.K, d.Np, d.Kp, const_cast<void*>(packed), const_cast<void*>(scales), canon_codes,
+               canon_scales};
+  return hip_status(q4::launch_w8_to_canonical(a, static_cast<hipStream_t>(stream)), "q8 to_canonical launch");
+}
+
+q4_status q8_from_canonical(const void* canon_codes, const void* canon_scales, int64_t out, int64_t in,
+                            void* packed, void* scales, void* stream) {
+  if (!packed || !scales || !canon_codes || !canon_scales) return fail(Q4_ERR_NULL, "a required pointer is NULL");
+  Dims d;
+  q4_status st = check_w8_dims(out, in, &d);
+  if (st != Q4_OK) return st;
+  if (!aligned(packed, 4) || !aligned(scales, 2) || !aligned(canon_scales, 2))
+    return fail(Q4_ERR_ALIGN, "packed needs 4-byte, scales 2-byte alignment");
+  q4::W8Args a{nullptr, d.N, d.K, d.Np, d.Kp, packed, scales, const_cast<void*>(canon_codes),
+               const_cast<void*>(canon_scales)};
+  return hip_status(q4::launch_w8_from_canonical(a, static_cast<hipStream_t>(stream)), "q8 from_canonical launch");
 }
 
 }  // extern "C"

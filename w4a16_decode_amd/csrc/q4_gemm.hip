@@ -59,9 +59,9 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 // the chunks in chunk order, so the result does not depend on which wavefront ran
 // which unit. With KS > 1 the workgroups write float32 partials to the workspace
 // and reduce_splits_kernel adds them in a fixed order.
-template <int R, int GSUB, bool ASYM>
+template <int R, int GSUB, bool ASYM, int NW = 1>
 struct WStage {
-  uint4 w[R];
+  uint4 w[R][NW];  // NW 16-byte pieces of codes per lane and block (1: INT4, 2: INT8)
   uint2 sc[R][GSUB];
   uint32_t z[R][GSUB];
   int s;     // block index (uniform)
@@ -83,13 +83,30 @@ struct GemvLds {
 };
 
 // Wavefronts per workgroup the kernel is built for: 16 (one workgroup per CU,
-// 128 VGPRs) for one group per block and R <= 2, else 8 (256 VGPRs) so that the
-// extra scales and row tiles stay in registers.
-template <int R, int GSUB>
-constexpr int gemv_max_waves() { return (GSUB > 1 || R > 2) ? 8 : 16; }
+// 128 VGPRs) for one group per block and R <= 2 (R = 1 for INT8 codes), else 8
+// (256 VGPRs) so that the extra scales, row tiles or code pieces stay in registers.
+template <int R, int GSUB, bool Q8 = false>
+constexpr int gemv_max_waves() { return (GSUB > 1 || R > 2 || (Q8 && R > 1)) ? 8 : 16; }
 
-template <int R, int GSUB, bool ASYM, int P, int XCH>
-__global__ __launch_bounds__((gemv_max_waves<R, GSUB>() * 64))
+// Eight INT8 codes of the W8A16 layout (two dwords, four offset-binary bytes
+// b = q + 128 each, channel order) -> the float16 operand 1024 + b = 1152 + q:
+// v_perm_b32 interleaves the code bytes with the exponent byte 0x64 (1024.0h),
+// one instruction per pair. The GEMV subtracts 1152 * sum(x) per block.
+__device__ __forceinline__ half8_t magic8_i8(uint32_t d0, uint32_t d1) {
+  constexpr uint32_t kExp = 0x64646464u;
+  const uint32_t p0 = __builtin_amdgcn_perm(kExp, d0, 0x04010400u);
+  const uint32_t p1 = __builtin_amdgcn_perm(kExp, d0, 0x04030402u);
+  const uint32_t p2 = __builtin_amdgcn_perm(kExp, d1, 0x04010400u);
+  const uint32_t p3 = __builtin_amdgcn_perm(kExp, d1, 0x04030402u);
+  return __builtin_bit_cast(half8_t, make_uint4(p0, p1, p2, p3));
+}
+
+// Q8: W8A16 codes (per-row INT8 scale passed as one group spanning the row, J = S,
+// Gp = 1): a 16-row x 128-channel block is 2 KiB, two 1 KiB halves of 64 channels;
+// lane l's 16 bytes of half h hold row l%16, channels 64h + 32j + 8(l/16) + e at
+// byte 8j + e (j = 0, 1; e = 0..7), so each half feeds two MFMA steps.
+template <int R, int GSUB, bool ASYM, int P, int XCH, bool Q8 = false>
+__global__ __launch_bounds__((gemv_max_waves<R, GSUB, Q8>() * 64))
 void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
                  const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int T,
                  int S, int Gp, int J, int KS, int nRB, int CH, uint16_t* __restrict__ y,
@@ -101,6 +118,9 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
   // one partial covers (128 / GSUB).
   constexpr bool BIAS = !ASYM;
   constexpr int UNIT = kSuperK / GSUB;
+  constexpr int NW = Q8 ? 2 : 1;        // 16-byte code pieces per lane and block
+  constexpr size_t BLK = 1024 * NW;     // bytes of one 16 x 128 block
+  static_assert(!Q8 || (GSUB == 1 && !ASYM), "INT8 codes are symmetric with one scale per row");
   const int W = blockDim.x >> 6;
   // readfirstlane: the wavefront index is uniform, and saying so keeps every value
   // derived from it in scalar registers
@@ -171,7 +191,7 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const size_t tile = (size_t)min(rb * R + r, T - 1);
-      l_wt[r] = pk + tile * S * 1024;
+      l_wt[r] = pk + tile * S * BLK;
       l_st[r] = reinterpret_cast<const unsigned char*>(scales) + tile * Gp * 32;
     }
   };
@@ -185,11 +205,13 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
       l_st[r] = reinterpret_cast<const unsigned char*>(scales);
     }
   }
-  auto load = [&](WStage<R, GSUB, ASYM>& st) __attribute__((always_inline)) {
+  auto load = [&](WStage<R, GSUB, ASYM, NW>& st) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const unsigned char* wp = l_wt[r] + (size_t)min(l_s, S - 1) * 1024 + w_lane;
-      st.w[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp)));
+      const unsigned char* wp = l_wt[r] + (size_t)min(l_s, S - 1) * BLK + w_lane;
+#pragma unroll
+      for (int h = 0; h < NW; ++h)
+        st.w[r][h] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + 1024 * h)));
 #pragma unroll
       for (int gs = 0; gs < GSUB; ++gs) {
         const size_t goff = (size_t)(l_j + gs) * 32;
@@ -215,7 +237,7 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
       l_j += GSUB;
     }
   };
-  WStage<R, GSUB, ASYM> buf[P];
+  WStage<R, GSUB, ASYM, NW> buf[P];
 #pragma unroll
   for (int p = 0; p < P - 1; ++p) load(buf[p]);
 
@@ -234,12 +256,15 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
     const int c8 = idx - b * row_chunks;
     uint4 v = (real && wsb0 * kSuperK + c8 * 8 < K) ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
     if (BIAS) {
+      // INT8 codes keep x as it is: bias 1152 * sum(x) (magic8_i8)
       half8_t h = as_half8(v);
-      h[2] *= (_Float16)0.0625f;
-      h[3] *= (_Float16)0.0625f;
-      h[6] *= (_Float16)0.0625f;
-      h[7] *= (_Float16)0.0625f;
-      v = __builtin_bit_cast(uint4, h);
+      if (!Q8) {
+        h[2] *= (_Float16)0.0625f;
+        h[3] *= (_Float16)0.0625f;
+        h[6] *= (_Float16)0.0625f;
+        h[7] *= (_Float16)0.0625f;
+        v = __builtin_bit_cast(uint4, h);
+      }
       float plain = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
       float scaled = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
 #pragma unroll
@@ -247,7 +272,8 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
         plain += __shfl_xor(plain, m);
         scaled += __shfl_xor(scaled, m);
       }
-      if (real && c8 % CPU == 0) beta[b * nunits + c8 / CPU] = 1032.f * plain + 1152.f * scaled;
+      if (real && c8 % CPU == 0)
+        beta[b * nunits + c8 / CPU] = Q8 ? 1152.f * (plain + scaled) : 1032.f * plain + 1152.f * scaled;
     }
     if (real) *reinterpret_cast<uint4*>(xl + b * xstride + c8 * 8) = v;
   }
@@ -283,7 +309,7 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
   };
   read_x(buf[0].s);
 
-  auto compute = [&](const WStage<R, GSUB, ASYM>& st, int s_next) __attribute__((always_inline)) {
+  auto compute = [&](const WStage<R, GSUB, ASYM, NW>& st, int s_next) __attribute__((always_inline)) {
     half8_t xc[4];
     float bc[GSUB];
 #pragma unroll
@@ -297,10 +323,18 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
       for (int gs = 0; gs < GSUB; ++gs) {
         const half4_t sh = __builtin_bit_cast(half4_t, st.sc[r][gs]);
         float4_t part = {0.f, 0.f, 0.f, 0.f};
-        if (BIAS) {
+        if (Q8) {
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            const uint4& v = st.w[r][mm >> 1];
+            part = mfma16x16x32(magic8_i8(lane_dword(v, 2 * (mm & 1)), lane_dword(v, 2 * (mm & 1) + 1)), xc[mm], part);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf((float)sh[i], part[i] - bc[gs], acc[r][i]);
+        } else if (BIAS) {
 #pragma unroll
           for (int mm = 0; mm < MPG; ++mm)
-            part = mfma16x16x32(magic8r(lane_dword(st.w[r], gs * MPG + mm), dq), xc[gs * MPG + mm], part);
+            part = mfma16x16x32(magic8r(lane_dword(st.w[r][0], gs * MPG + mm), dq), xc[gs * MPG + mm], part);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf((float)sh[i], part[i] - bc[gs], acc[r][i]);
         } else {
@@ -309,7 +343,7 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
           const half2_t bhi = {(_Float16)-64.0f - z, (_Float16)-64.0f - z};
 #pragma unroll
           for (int mm = 0; mm < MPG; ++mm)
-            part = mfma16x16x32(dequant8r(lane_dword(st.w[r], gs * MPG + mm), dq, blo, bhi), xc[gs * MPG + mm], part);
+            part = mfma16x16x32(dequant8r(lane_dword(st.w[r][0], gs * MPG + mm), dq, blo, bhi), xc[gs * MPG + mm], part);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf((float)sh[i], part[i], acc[r][i]);
         }
@@ -678,19 +712,20 @@ int device_cus() {
   return cus;
 }
 
-template <int R, int GSUB, bool ASYM, int XCH>
+template <int R, int GSUB, bool ASYM, int XCH, bool Q8 = false>
 hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
-  // pipeline depth (blocks of codes in flight + 1) per row-tile count
-  constexpr int P = R == 1 ? 8 : 4;
+  // pipeline depth (blocks of codes in flight + 1) per row-tile count; INT8
+  // blocks are twice as large
+  constexpr int P = Q8 ? (R == 1 ? 5 : 3) : (R == 1 ? 8 : 4);
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
-  const int W = std::min(a.waves_per_group, gemv_max_waves<R, GSUB>());
+  const int W = std::min(a.waves_per_group, gemv_max_waves<R, GSUB, Q8>());
   const int KS = a.k_splits;
   const int nRB = (T + R - 1) / R;
   const int max_nsb = (S + KS - 1) / KS;
   const int min_nsb = S / KS;  // >= 1: the host keeps KS <= S
-  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>);
   const size_t lim = a.lds_limit;
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, 0).total;
@@ -717,7 +752,7 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   CH = std::max(CH, 1);
   const size_t lds = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, n_rb * CH).total;
   const int grid = (int)(per_split * KS);
-  hipLaunchKernelGGL((gemv_kernel<R, GSUB, ASYM, P, XCH>), dim3(grid), dim3(W * kWave), lds, stream,
+  hipLaunchKernelGGL((gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>), dim3(grid), dim3(W * kWave), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
                      a.Gp, J, KS, nRB, CH, static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
@@ -733,14 +768,14 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
 
 // x chunks of 16 bytes each thread copies: the fewest of 2, 4, 8 that cover the
 // activation slice of the largest split
-template <int R, int GSUB, bool ASYM>
+template <int R, int GSUB, bool ASYM, bool Q8 = false>
 hipError_t launch_gemv_x(const GemmArgs& a, hipStream_t stream) {
-  const int W = std::min(a.waves_per_group, gemv_max_waves<R, GSUB>());
+  const int W = std::min(a.waves_per_group, gemv_max_waves<R, GSUB, Q8>());
   const int64_t max_nsb = (a.Kp / kSuperK + a.k_splits - 1) / a.k_splits;
   const int64_t per_thread = ((int64_t)a.B * max_nsb * 16 + W * kWave - 1) / (W * kWave);
-  if (per_thread <= 2) return launch_gemv_t<R, GSUB, ASYM, 2>(a, stream);
-  if (per_thread <= 4) return launch_gemv_t<R, GSUB, ASYM, 4>(a, stream);
-  return launch_gemv_t<R, GSUB, ASYM, 8>(a, stream);
+  if (per_thread <= 2) return launch_gemv_t<R, GSUB, ASYM, 2, Q8>(a, stream);
+  if (per_thread <= 4) return launch_gemv_t<R, GSUB, ASYM, 4, Q8>(a, stream);
+  return launch_gemv_t<R, GSUB, ASYM, 8, Q8>(a, stream);
 }
 
 template <int R, bool ASYM>
@@ -806,6 +841,13 @@ bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
 namespace {
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
+  if (a.q8) {
+    switch (a.rows_per_wave) {
+      case 1: return launch_gemv_x<1, 1, false, true>(a, stream);
+      case 2: return launch_gemv_x<2, 1, false, true>(a, stream);
+      default: return launch_gemv_x<4, 1, false, true>(a, stream);
+    }
+  }
   if (gemv_streams_x(a.B, a.Kp, a.rows_per_wave, a.k_splits)) return launch_gemv_stream_a<2>(a, stream);
   switch (a.rows_per_wave) {
     case 1: return launch_gemv_a<1>(a, stream);

@@ -39,6 +39,7 @@ struct GemmArgs {
   const void* scales;
   const void* zeros;
   bool asym;
+  bool q8;  // per-channel INT8 codes (B <= 16 GEMV only); group = Kp, Gp = 1
   int N, K, group;
   int Np, Kp, Gp;
   void* y;
@@ -52,7 +53,20 @@ struct GemmArgs {
   size_t lds_limit;     // B <= 16: LDS a workgroup may use (sizes the per-workgroup result buffer)
 };
 
+// Per-channel INT8 (W8A16): codes [Np * Kp] bytes in 2 KiB blocks, scales float16 [Np].
+struct W8Args {
+  const void* W;  // float16 [N, K] (quantize)
+  int N, K, Np, Kp;
+  void* packed;
+  void* scales;
+  void* canon_codes;   // int8 [N, K]
+  void* canon_scales;  // float16 [N]
+};
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_quantize_w8(const W8Args& a, hipStream_t stream);
+hipError_t launch_w8_to_canonical(const W8Args& a, hipStream_t stream);
+hipError_t launch_w8_from_canonical(const W8Args& a, hipStream_t stream);
 hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);

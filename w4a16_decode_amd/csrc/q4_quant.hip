@@ -283,6 +283,110 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
   }
 }
 
+// ---- per-channel INT8 (W8A16) -------------------------------------------------
+//
+// Symmetric INT8 with one scale per output channel: s = row amax / 127,
+// q = clamp(round(w / s), -127, 127) ("量化：PTQ、GPTQ、AWQ 与 SmoothQuant",
+// charles2530.github.io, the closing quick code example; "模型量化技术工程实践",
+// www.iopencloud.com, section 2.1). Two passes: the row amax needs the whole row
+// before any code. w8_scale_kernel: one wavefront per row (rows past N get scale
+// 0); w8_pack_kernel: one wavefront per 16-row x 128-channel block, which it
+// writes as two 1 KiB halves (lane l = r + 16c stores row r, channels
+// 64h + 32j + 8c + e at byte 8j + e of its 16 bytes in half h), codes offset by 128.
+
+__global__ __launch_bounds__(256) void w8_scale_kernel(const uint16_t* __restrict__ W, int N, int K, int Np,
+                                                       uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t n = wave; n < Np; n += nwaves) {
+    float a = 0.0f;
+    if (n < N) {
+      const uint16_t* row = W + (size_t)n * K;  // K % 8 == 0: 16-byte aligned rows
+#pragma unroll 4
+      for (int k = lane * 8; k < K; k += kWave * 8) {
+        const half8_t h = as_half8(*reinterpret_cast<const uint4*>(row + k));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf((float)h[e]));
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
+    if (lane == 0) scales[n] = half_bits((_Float16)(a / 127.0f));
+  }
+}
+
+__device__ __forceinline__ uint32_t w8_code(float w, float s) {
+  // offset-binary byte q + 128, q = clamp(rint(w / s), -127, 127); code 0 for s == 0
+  if (s == 0.0f) return 128u;
+  const float q = fminf(fmaxf(rintf(w / s), -127.0f), 127.0f);
+  return (uint32_t)((int)q + 128);
+}
+
+__global__ __launch_bounds__(256) void w8_pack_kernel(const uint16_t* __restrict__ W, int N, int K, int S,
+                                                      int64_t units, const uint16_t* __restrict__ scales,
+                                                      uint4* __restrict__ packed) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t u = wave; u < units; u += nwaves) {
+    const int t = (int)(u / S), s = (int)(u % S);
+    const int n = t * kTileRows + r;
+    const float sf = (float)__builtin_bit_cast(_Float16, scales[n]);
+    uint32_t d[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        d[2 * m + i] = w8_code(w.v[4 * i], sf) | (w8_code(w.v[4 * i + 1], sf) << 8) |
+                       (w8_code(w.v[4 * i + 2], sf) << 16) | (w8_code(w.v[4 * i + 3], sf) << 24);
+    }
+    uint4* out = packed + ((size_t)t * S + s) * 2 * kWave + lane;
+    out[0] = make_uint4(d[0], d[1], d[2], d[3]);
+    out[kWave] = make_uint4(d[4], d[5], d[6], d[7]);
+  }
+}
+
+__device__ __forceinline__ size_t w8_dev_byte(int n, int k, int S) {
+  const int t = n >> 4, r = n & 15, s = k >> 7, h = (k & 127) >> 6, j = (k & 63) >> 5, c = (k & 31) >> 3;
+  return (((size_t)t * S + s) * 2 + h) * 1024 + (size_t)(r + 16 * c) * 16 + 8 * j + (k & 7);
+}
+
+__global__ void w8_to_canonical_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+                                       int N, int K, int S, int8_t* __restrict__ canon,
+                                       uint16_t* __restrict__ canon_scales) {
+  const int64_t total = (int64_t)N * K;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / K), k = (int)(i % K);
+    canon[i] = (int8_t)((int)packed[w8_dev_byte(n, k, S)] - 128);
+    if (k == 0) canon_scales[n] = scales[n];
+  }
+}
+
+__global__ void w8_from_canonical_kernel(const int8_t* __restrict__ canon, const uint16_t* __restrict__ canon_scales,
+                                         int N, int K, int S, int Np, int64_t dwords, uint32_t* __restrict__ packed,
+                                         uint16_t* __restrict__ scales) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < dwords; i += (int64_t)gridDim.x * blockDim.x) {
+    // dword i: block (t, s), half h, lane l, dword d of the lane's 16 bytes
+    const int d = (int)(i & 3), l = (int)((i >> 2) & 63), h = (int)((i >> 8) & 1);
+    const int64_t ts = i >> 9;
+    const int t = (int)(ts / S), s = (int)(ts % S);
+    const int n = t * 16 + (l & 15);
+    const int k0 = s * 128 + 64 * h + 32 * (d >> 1) + 8 * (l >> 4) + 4 * (d & 1);
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k0 + e;
+      const uint32_t b = (n < N && k < K) ? (uint32_t)((int)canon[(size_t)n * K + k] + 128) : 128u;
+      v |= b << (8 * e);
+    }
+    packed[i] = v;
+    if (i < Np) scales[i] = i < N ? canon_scales[i] : (uint16_t)0;
+  }
+}
+
 // ---- layout converters -------------------------------------------------------
 
 __device__ __forceinline__ size_t dev_dword_index(int n, int k, int S) {
@@ -439,6 +543,37 @@ hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((groups_from_canonical_kernel<uint8_t>), dim3(grid_for(gtotal, block)), dim3(block), 0, stream,
                        static_cast<const uint8_t*>(a.canon_zeros), a.N, G, a.Gp, gtotal,
                        static_cast<uint8_t*>(a.zeros));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_w8(const W8Args& a, hipStream_t stream) {
+  const int S = a.Kp / kSuperK;
+  const int T = a.Np / kTileRows;
+  const int block = 256;
+  hipLaunchKernelGGL(w8_scale_kernel, dim3(grid_for((int64_t)a.Np * kWave, block)), dim3(block), 0, stream,
+                     static_cast<const uint16_t*>(a.W), a.N, a.K, a.Np, static_cast<uint16_t*>(a.scales));
+  const int64_t units = (int64_t)T * S;
+  hipLaunchKernelGGL(w8_pack_kernel, dim3(grid_for(units * kWave, block)), dim3(block), 0, stream,
+                     static_cast<const uint16_t*>(a.W), a.N, a.K, S, units, static_cast<const uint16_t*>(a.scales),
+                     static_cast<uint4*>(a.packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_w8_to_canonical(const W8Args& a, hipStream_t stream) {
+  const int block = 256;
+  hipLaunchKernelGGL(w8_to_canonical_kernel, dim3(grid_for((int64_t)a.N * a.K, block)), dim3(block), 0, stream,
+                     static_cast<const uint8_t*>(a.packed), static_cast<const uint16_t*>(a.scales), a.N, a.K,
+                     a.Kp / kSuperK, static_cast<int8_t*>(a.canon_codes), static_cast<uint16_t*>(a.canon_scales));
+  return hipGetLastError();
+}
+
+hipError_t launch_w8_from_canonical(const W8Args& a, hipStream_t stream) {
+  const int block = 256;
+  const int64_t dwords = (int64_t)a.Np * a.Kp / 4;
+  hipLaunchKernelGGL(w8_from_canonical_kernel, dim3(grid_for(dwords, block)), dim3(block), 0, stream,
+                     static_cast<const int8_t*>(a.canon_codes), static_cast<const uint16_t*>(a.canon_scales), a.N,
+                     a.K, a.Kp / kSuperK, a.Np, dwords, static_cast<uint32_t*>(a.packed),
+                     static_cast<uint16_t*>(a.scales));
   return hipGetLastError();
 }
 

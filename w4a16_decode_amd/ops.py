@@ -245,3 +245,107 @@ def from_canonical(codes, scales, group: int, zeros=None) -> QuantizedWeight:
                                qw.zeros.data_ptr() if asym else None, _stream(codes))
     _check(st)
     return qw
+
+
+# ---- per-channel INT8 weights (W8A16), include/q8.h ------------------------------
+
+
+@dataclass
+class QuantizedWeight8:
+    """Device-layout per-channel INT8 weights of an [out_features, in_features] matrix."""
+
+    packed: object          # uint8 [q8_packed_bytes(out, in)]
+    scales: object          # float16 [q8_scales_count(out)]
+    out_features: int
+    in_features: int
+
+    @property
+    def device(self):
+        return self.packed.device
+
+    def nbytes(self) -> int:
+        return self.packed.numel() + 2 * self.scales.numel()
+
+
+def q8_packed_bytes(out_features: int, in_features: int) -> int:
+    return int(_lib.load().q8_packed_bytes(out_features, in_features))
+
+
+def q8_workspace_bytes(batch: int, out_features: int, in_features: int) -> int:
+    return int(_lib.load().q8_workspace_bytes(batch, out_features, in_features))
+
+
+def _alloc_qw8(out_features: int, in_features: int, device) -> QuantizedWeight8:
+    import torch
+
+    lib = _lib.load()
+    nb = int(lib.q8_packed_bytes(out_features, in_features))
+    ns = int(lib.q8_scales_count(out_features))
+    if nb == 0 or ns == 0:
+        raise Q4Error(2, f"invalid shape [{out_features}, {in_features}] (in must be a positive multiple of 8)")
+    return QuantizedWeight8(torch.empty(nb, dtype=torch.uint8, device=device),
+                            torch.empty(ns, dtype=torch.float16, device=device), out_features, in_features)
+
+
+def q8_quantize_pack(W) -> QuantizedWeight8:
+    """q8_quantize_pack: per-row symmetric INT8 of a float16 [out, in] GPU tensor."""
+    import torch
+
+    _require_gpu(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [out_features, in_features]")
+    out_features, in_features = W.shape
+    qw = _alloc_qw8(out_features, in_features, W.device)
+    _check(_lib.load().q8_quantize_pack(W.data_ptr(), out_features, in_features, qw.packed.data_ptr(),
+                                        qw.scales.data_ptr(), _stream(W)))
+    return qw
+
+
+def q8_gemm(x, qw: QuantizedWeight8, out=None, workspace=None):
+    """q8_gemm: y = x . (q * s)^T, float16 [B, out_features]."""
+    B, out = _prep_gemm(x, qw, out)
+    lib = _lib.load()
+    need = int(lib.q8_workspace_bytes(B, qw.out_features, qw.in_features)) if B > 0 else 0
+    ws_ptr, ws_bytes = _workspace(x, need, workspace)
+    _check(lib.q8_gemm(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.out_features,
+                       qw.in_features, out.data_ptr(), ws_ptr, ws_bytes, _stream(x)))
+    return out
+
+
+def q8_gemm_config(x, qw: QuantizedWeight8, rows_per_wave: int, waves_per_group: int, k_splits: int = 1, out=None,
+                   workspace=None):
+    """q8_gemm_config: q8_gemm with an explicit GEMV launch shape (tuning)."""
+    B, out = _prep_gemm(x, qw, out)
+    need = 4 * k_splits * min(B, 16) * qw.out_features if k_splits > 1 else 0
+    ws_ptr, ws_bytes = _workspace(x, need, workspace)
+    _check(_lib.load().q8_gemm_config(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.out_features,
+                                      qw.in_features, out.data_ptr(), rows_per_wave, waves_per_group, k_splits,
+                                      ws_ptr, ws_bytes, _stream(x)))
+    return out
+
+
+def q8_to_canonical(qw: QuantizedWeight8):
+    """q8_to_canonical: (codes int8 [out, in], scales float16 [out])."""
+    import torch
+
+    N, K = qw.out_features, qw.in_features
+    codes = torch.empty((N, K), dtype=torch.int8, device=qw.device)
+    scales = torch.empty(N, dtype=torch.float16, device=qw.device)
+    _check(_lib.load().q8_to_canonical(qw.packed.data_ptr(), qw.scales.data_ptr(), N, K, codes.data_ptr(),
+                                       scales.data_ptr(), _stream(qw.packed)))
+    return codes, scales
+
+
+def q8_from_canonical(codes, scales) -> QuantizedWeight8:
+    """q8_from_canonical: canonical int8 codes [out, in] and float16 scales [out] -> device layout."""
+    import torch
+
+    _require_gpu(codes, "codes", torch.int8)
+    _require_gpu(scales, "scales", torch.float16)
+    N, K = codes.shape
+    if tuple(scales.shape) != (N,):
+        raise ValueError("scales must be [out]")
+    qw = _alloc_qw8(N, K, codes.device)
+    _check(_lib.load().q8_from_canonical(codes.data_ptr(), scales.data_ptr(), N, K, qw.packed.data_ptr(),
+                                         qw.scales.data_ptr(), _stream(codes)))
+    return qw

@@ -43,6 +43,16 @@ def quantize_bytes(out_features: int, in_features: int, group: int, asym: bool =
     return 2 * out_features * in_features + weight_bytes(out_features, in_features, group, asym)
 
 
+def w8_weight_bytes(out_features: int, in_features: int) -> int:
+    """Per-channel INT8 codes (1 byte each) + one float16 scale per row."""
+    return out_features * in_features + 2 * out_features
+
+
+def w8_gemm_read_bytes(B: int, out_features: int, in_features: int) -> int:
+    """Bytes the W8A16 product must read: INT8 weights, row scales, float16 activations."""
+    return w8_weight_bytes(out_features, in_features) + 2 * B * in_features
+
+
 def time_model_s(w_bytes: float, n_params: float, m: int, bw_bytes_s: float, flops_s: float) -> float:
     """T(m) = max(W_bytes / BW, 2 N m / F): lower bound of one forward over m token rows."""
     return max(w_bytes / bw_bytes_s, 2.0 * n_params * m / flops_s)
