@@ -145,11 +145,13 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     // extra tile per load keeps more bytes in flight where there are few row
     // blocks), else one: tall matrices, small groups (several scales per block) and
     // matrices so small that two tiles per row block would leave CUs idle
-    // (INT8 codes: always one; a 2 KiB block per tile already keeps 8 KiB in flight)
+    // (INT8 codes: always one; 2 KiB blocks already keep 6 KiB per wavefront in flight)
     const int R = (a->q8 || T >= 2048 || d.group < 128 || T > S * 8 || T < 512) ? 1 : 2;
     // 8 wavefronts (two workgroups per CU) stream best for B <= 4; 16 hold twice
     // the activation slice, which keeps larger batches from splitting the channels
-    const int W = B <= 4 ? 8 : gemv_max_waves(R, d.group, a->q8);
+    // (INT8 codes on fewer than 1024 row tiles of at most 8192 channels at B <= 2: 4
+    // wavefronts, twice the workgroups, longer units per wavefront)
+    const int W = (a->q8 && B <= 2 && T < 1024 && S <= 64) ? 4 : B <= 4 ? 8 : gemv_max_waves(R, d.group, a->q8);
     int KS = 1;
     while (KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
     a->rows_per_wave = R;

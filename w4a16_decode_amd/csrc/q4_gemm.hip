@@ -716,7 +716,7 @@ template <int R, int GSUB, bool ASYM, int XCH, bool Q8 = false>
 hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   // pipeline depth (blocks of codes in flight + 1) per row-tile count; INT8
   // blocks are twice as large
-  constexpr int P = Q8 ? (R == 1 ? 5 : 3) : (R == 1 ? 8 : 4);
+  constexpr int P = Q8 ? (R == 1 ? 4 : 3) : (R == 1 ? 8 : 4);
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
