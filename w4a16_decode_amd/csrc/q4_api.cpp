@@ -148,10 +148,12 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     // (INT8 codes: always one; 2 KiB blocks already keep 6 KiB per wavefront in flight)
     const int R = (a->q8 || T >= 2048 || d.group < 128 || T > S * 8 || T < 512) ? 1 : 2;
     // 8 wavefronts (two workgroups per CU) stream best for B <= 4; 16 hold twice
-    // the activation slice, which keeps larger batches from splitting the channels
-    // (INT8 codes on fewer than 1024 row tiles of at most 8192 channels at B <= 2: 4
-    // wavefronts, twice the workgroups, longer units per wavefront)
-    const int W = (a->q8 && B <= 2 && T < 1024 && S <= 64) ? 4 : B <= 4 ? 8 : gemv_max_waves(R, d.group, a->q8);
+    // the activation slice, which keeps larger batches from splitting the channels.
+    // At B <= 2 on short rows (<= 4096 channels; INT8 codes: <= 8192 channels and
+    // fewer than 1024 row tiles) 4 wavefronts: twice the workgroups, and units long
+    // enough that every wavefront keeps streaming.
+    const bool w4 = B <= 2 && (S <= 32 || (a->q8 && T < 1024 && S <= 64));
+    const int W = w4 ? 4 : B <= 4 ? 8 : gemv_max_waves(R, d.group, a->q8);
     int KS = 1;
     while (KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
     a->rows_per_wave = R;
