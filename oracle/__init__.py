@@ -18,15 +18,19 @@ Sources, cited by page title and section throughout:
        part 03 of the efficient-inference series) -- section 二.2 (quantization
        form, granularity, bits per weight), 二.3 (W4A16 dataflow), 三.1 (step
        alpha/7 and the Delta^2/12 noise model), 三.2 (clipping vs rounding, the
-       range search), 六.2 (the four-weight RTN/AWQ table), 八.2 (41.86 -> scale
-       5.9805).
+       range search), 四.3 (INT8 per-channel RTN as the W8A16 default), 五.3
+       (act-order and g_idx), 六.2 (the four-weight RTN/AWQ table), 七.1 and 七.5
+       (the INT8 step and its error), 八.2 (41.86 -> scale 5.9805), 十一.2 (the
+       g_idx reorder is a gather).
 [WIKI] "压缩算法" (cs-knowledge-wiki.pages.dev) -- section 7.4.1.1 (asymmetric
        s = (max-min)/(2^b-1), z = round(-min/s)), 7.4.1.2 (INT4 group code,
        clamp [-8, 7], two INT4 codes packed into one byte).
 [IOC]  "模型量化技术工程实践：GPTQ/AWQ/QLoRA深度解析" (www.iopencloud.com) --
-       section 1.2 (worked rounding example 3.14159 at scale 0.01).
+       section 1.2 (worked rounding example 3.14159 at scale 0.01; clipping 1000
+       to the INT8 range), 2.1 (symmetric INT8, scale max/127).
 [CH]   "量化：PTQ、GPTQ、AWQ 与 SmoothQuant" (charles2530.github.io) --
-       section 1 (unified affine form, 4-bit symmetric range {-8..7}).
+       section 1 (unified affine form, 4-bit symmetric range {-8..7}); the
+       closing quick code example (per-channel INT8).
 
 Readings taken where the pages are silent or inconsistent are listed in the
 docstrings of the functions that take them.
@@ -58,6 +62,7 @@ from .layout import (  # noqa: F401
 )
 from .gemm import gemm_ref, gemm_ref_rows, to_fp16  # noqa: F401
 from .clip import clip_scale_fp16, clip_codes, clip_errors, quantize_sym_clip  # noqa: F401
+from .actorder import actorder_order, actorder_gidx, quantize_sym_actorder, dequant_gidx, gemm_gidx_rows  # noqa: F401
 from .w8 import (  # noqa: F401
     w8_scale_fp16,
     w8_codes,

@@ -9,7 +9,7 @@ Weights are drawn as N(0, 1) in float32, multiplied by 0.02 and cast to
 float16 with round-to-nearest-even; activations are N(0, 1) cast to float16.
 Host streams come from ``numpy.random.default_rng(SeedSequence([seed, layer,
 matrix, stream]))`` (stream 0 = weights, 1 = activations, 2 = outlier column
-choice). Large sweeps generate weights on the device with a seeded
+choice, 3 = per-channel energies ordering act-order groups). Large sweeps generate weights on the device with a seeded
 ``torch.Generator``; :func:`device_weight` documents that recipe.
 """
 
@@ -70,6 +70,13 @@ def heavy_tailed_weight(out_features: int, in_features: int, seed: int = 5, df: 
     cols = np.sort(_rng(seed, layer, matrix, 2).choice(in_features, size=n_out, replace=False))
     w[:, cols] *= np.float32(outlier_gain)
     return w.astype(np.float16), cols
+
+
+def channel_energy(in_features: int, seed: int = 0, layer: int = 0, matrix: int = 0) -> np.ndarray:
+    """Synthetic stand-in for a calibration statistic per input channel (the Hessian
+    diagonal that orders the act-order groups): log-normal(0, 1) float64 values
+    from stream 3. No calibration data is involved."""
+    return _rng(seed, layer, matrix, 3).lognormal(0.0, 1.0, size=in_features)
 
 
 def activation(batch: int, in_features: int, seed: int = 0, layer: int = 0, matrix: int = 0) -> np.ndarray:

@@ -697,4 +697,105 @@ def pin_w8_product_bruteforce(seed=34):
                 assert abs(y[b, i] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
 
 
+# ------------------------------- act-order groups with g_idx (oracle/actorder.py)
+
+
+def pin_actorder_constant_h_is_rtn(seed=41):
+    """Equal H_ii everywhere keeps the channel order: act-order is plain RTN, g_idx = k // g."""
+    o = _orc()
+    for g in (32, 128):
+        W = synth.weight(24, 512, seed=seed + g)
+        q, s, gi = o.quantize_sym_actorder(W, g, np.ones(512))
+        q0, s0 = o.quantize_sym(W, g)
+        assert np.array_equal(q, q0) and np.array_equal(s.view(np.uint16), s0.view(np.uint16))
+        assert np.array_equal(gi, np.arange(512) // g)
+
+
+def pin_actorder_hand_example():
+    """K = 8, g = 4 worked by hand. h = [0.1, 5, 0.3, 2, 2, 0.2, 9, 2]: descending
+    order 6, 1, 3, 4 | 7, 2, 5, 0 (the three-way tie at 2 keeps channels 3 and 4
+    before 7, across the group boundary), so
+    g_idx = [1, 0, 1, 0, 0, 1, 0, 1]. Row [0.5, -7, 1, 3.5, 2, -0.25, 0.75, 3.5]:
+    group 0 {-7, 3.5, 2, 0.75} has amax 7, scale 1, codes -7, 4 (tie to even), 2, 1;
+    group 1 {0.5, 1, -0.25, 3.5} has amax 3.5, scale 0.5, codes 1, 2, 0 (-0.5 to even), 7."""
+    o = _orc()
+    h = np.array([0.1, 5, 0.3, 2, 2, 0.2, 9, 2])
+    assert o.actorder_order(h).tolist() == [6, 1, 3, 4, 7, 2, 5, 0]
+    W = np.array([[0.5, -7, 1, 3.5, 2, -0.25, 0.75, 3.5]], dtype=np.float16)
+    q, s, gi = o.quantize_sym_actorder(W, 4, h)
+    assert gi.tolist() == [1, 0, 1, 0, 0, 1, 0, 1]
+    assert s.tolist() == [[1.0, 0.5]]
+    assert q.tolist() == [[1, -7, 2, 4, 2, 0, 1, 7]]
+    assert o.dequant_gidx(q, s, gi).tolist() == [[0.5, -7, 1, 4, 2, 0, 1, 3.5]]
+    q0, _ = o.quantize_sym(W, 4)                  # contiguous groups give other codes
+    assert q0.tolist() != q.tolist()
+
+
+def pin_actorder_gidx_structure(seed=42):
+    """Every group holds exactly g channels, and every channel of group j has H_ii at
+    least that of every channel of group j + 1."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    for K, g in ((256, 32), (1024, 128), (384, 128)):
+        h = r.lognormal(size=K)
+        h[::7] = h[0]                               # ties
+        gi = o.actorder_gidx(h, g)
+        assert np.array_equal(np.bincount(gi, minlength=K // g), np.full(K // g, g))
+        for j in range(K // g - 1):
+            assert h[gi == j].min() >= h[gi == j + 1].max()
+
+
+def pin_actorder_channel_relabelling(seed=43):
+    """Relabelling the input channels of W and h together relabels the codes and leaves
+    the scales unchanged (groups follow the H_ii values, not the positions)."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    N, K, g = 16, 512, 64
+    W = synth.weight(N, K, seed=seed)
+    h = r.permutation(K).astype(np.float64)        # distinct values: no ties
+    sigma = r.permutation(K)
+    q, s, gi = o.quantize_sym_actorder(W, g, h)
+    q2, s2, gi2 = o.quantize_sym_actorder(np.ascontiguousarray(W[:, sigma]), g, h[sigma])
+    assert np.array_equal(q2, q[:, sigma]) and np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+    assert np.array_equal(gi2, gi[sigma])
+
+
+def pin_actorder_outlier_columns():
+    """With the 41 outlier input channels first in the order (largest H_ii) they share
+    group 0, and every other group keeps a small scale: on the ordinary channels the
+    weight error falls well below contiguous RTN's, where most groups hold an outlier;
+    the outliers themselves now share one coarse scale and carry more error."""
+    o = _orc()
+    W, cols = synth.heavy_tailed_weight(64, 4096, seed=5)
+    h = np.ones(4096)
+    h[cols] = 50.0
+    q, s, gi = o.quantize_sym_actorder(W, 128, h)
+    assert np.all(gi[cols] == 0) and np.count_nonzero(gi == 0) == 128
+    ordinary = np.ones(4096, dtype=bool)
+    ordinary[cols] = False
+    q0, s0 = o.quantize_sym(W, 128)
+    e_ao = (o.dequant_gidx(q, s, gi) - W.astype(np.float64)) ** 2
+    e_rtn = (o.dequant_sym(q0, s0, 128) - W.astype(np.float64)) ** 2
+    assert e_ao[:, ordinary].mean() < 0.25 * e_rtn[:, ordinary].mean()
+    assert e_ao[:, ~ordinary].mean() > e_rtn[:, ~ordinary].mean()
+
+
+def pin_actorder_product_bruteforce(seed=44):
+    """Exact rational y with each channel's scale looked up by hand from its group."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    for B, N, K, g in ((2, 5, 64, 16), (1, 9, 96, 32)):
+        W = synth.weight(N, K, seed=seed + N)
+        x = synth.activation(B, K, seed=seed + K)
+        h = r.lognormal(size=K)
+        q, s, gi = o.quantize_sym_actorder(W, g, h)
+        rank = sorted(range(K), key=lambda k: (-h[k], k))
+        group_of = {k: i // g for i, k in enumerate(rank)}
+        y = o.gemm_gidx_rows(x, q, s, gi, np.arange(N))
+        for b in range(B):
+            for n in range(N):
+                ex = sum(Fraction(float(x[b, k])) * Fraction(float(s[n, group_of[k]])) * int(q[n, k]) for k in range(K))
+                assert abs(y[b, n] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

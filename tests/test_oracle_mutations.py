@@ -13,6 +13,7 @@ import oracle.layout
 import oracle.rtn
 import oracle.clip
 import oracle.w8
+import oracle.actorder
 from pins import ALL_PINS
 
 
@@ -274,6 +275,40 @@ def _w8_dequant_rows_shifted(monkeypatch):
     monkeypatch.setattr(oracle, "dequant_w8", dq)
 
 
+def _actorder_ascending(monkeypatch):
+    monkeypatch.setattr(oracle.actorder, "actorder_order",
+                        lambda h: np.argsort(np.asarray(h, dtype=np.float64), kind="stable"))
+    monkeypatch.setattr(oracle, "actorder_order", oracle.actorder.actorder_order)
+
+
+def _actorder_gidx_inverted(monkeypatch):
+    def gidx(h, g):
+        order = oracle.actorder.actorder_order(h)
+        return order // g                                   # position -> group, not channel -> group
+
+    monkeypatch.setattr(oracle.actorder, "actorder_gidx", gidx)
+    monkeypatch.setattr(oracle, "actorder_gidx", gidx)
+
+
+def _actorder_ties_reversed(monkeypatch):
+    def order(h):
+        h = np.asarray(h, dtype=np.float64)
+        return np.lexsort((-np.arange(h.size), -h))                 # descending, ties by descending channel
+
+    monkeypatch.setattr(oracle.actorder, "actorder_order", order)
+    monkeypatch.setattr(oracle, "actorder_order", order)
+
+
+def _actorder_dequant_by_position(monkeypatch):
+    def dq(q, s16, g_idx):
+        q = np.asarray(q, dtype=np.float64)
+        g = q.shape[1] // np.asarray(s16).shape[1]
+        return q * np.repeat(np.asarray(s16, dtype=np.float64), g, axis=1)
+
+    monkeypatch.setattr(oracle.actorder, "dequant_gidx", dq)
+    monkeypatch.setattr(oracle, "dequant_gidx", dq)
+
+
 MUTATIONS = [
     _scale_div8, _scale_two_alpha_over_15, _truncate, _half_away, _fp16_quotient, _nibbles_swapped,
     _device_nibble_order, _device_lane_order, _dequant_wrong_group, _gemm_rows_reversed,
@@ -281,6 +316,7 @@ MUTATIONS = [
     _clip_ties_to_smaller, _clip_qmin8, _clip_error_on_codes, _clip_without_100,
     _w8_div128, _w8_clamp_m128, _w8_truncate, _w8_half_away, _w8_fp16_quotient, _w8_scale_per_column,
     _w8_layout_h_m_swapped, _w8_offset127, _w8_dequant_rows_shifted,
+    _actorder_ascending, _actorder_gidx_inverted, _actorder_ties_reversed, _actorder_dequant_by_position,
 ]
 
 
