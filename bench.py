@@ -367,6 +367,63 @@ def extras_w8(dev, int4_us_per_layer: float | None):
     return out
 
 
+def extras_actorder(dev, group: int):
+    """Act-order (g_idx) INT4 weights on the 70B layer's fused matrices: the product with
+    x gathered through perm against the plain product on the same shape, B in {1, 4, 32},
+    and the quantizer reading the columns through perm."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+    from w4a16_decode_amd import perfmodel
+
+    order = {name: i for i, name in enumerate(synth.MATRIX_ORDER)}
+    out = {}
+    for grp in synth.FUSED_GROUPS:
+        N = sum(synth.LLAMA3_70B[n][0] for n in grp)
+        K = synth.LLAMA3_70B[grp[0]][1]
+        copies = max(2, -(-300_000_000 // perfmodel.gemm_read_bytes(1, N, K, group)))
+        # a synthetic g_idx: every group gets `group` channels drawn at random
+        g_idx = np.random.default_rng(K).permutation(np.arange(K) // group).astype(np.int32)
+        perm = torch.from_numpy(q4.actorder_perm(g_idx, group)).to(dev)
+        plain, ao = [], []
+        for c in range(copies):
+            parts = [synth.device_weight(*synth.LLAMA3_70B[n], seed=3, layer=c, matrix=order[n], device=dev)
+                     for n in grp]
+            W = parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
+            del parts
+            plain.append(q4.quantize_pack(W, group))
+            if c == 0:
+                q4.quantize_pack_perm(W, group, perm)
+                torch.cuda.synchronize()
+                a, b = events()
+                a.record()
+                for _ in range(3):
+                    q4.quantize_pack_perm(W, group, perm)
+                b.record()
+                torch.cuda.synchronize()
+                tq = a.elapsed_time(b) / 1e3 / 3
+            ao.append(q4.quantize_pack_perm(W, group, perm))
+            del W
+        kind = KIND_OF["+".join(grp)]
+        res = {"shape": [N, K], "quantize_perm_us": round(tq * 1e6, 2)}
+        for B in (1, 4, 32):
+            x = synth.device_activation(B, K, seed=3, layer=0, matrix=100, device=dev)
+            y = torch.empty((B, N), dtype=torch.float16, device=dev)
+            ws = torch.empty(max(16, q4.workspace_bytes(B, N, K, group)), dtype=torch.uint8, device=dev)
+            wsp = torch.empty(max(16, q4.workspace_bytes_perm(B, N, K, group)), dtype=torch.uint8, device=dev)
+            t0 = graph_time(lambda: [q4.gemm(x, qw, out=y, workspace=ws) for qw in plain], 5) / copies
+            t1 = graph_time(lambda: [q4.gemm_perm(x, aw, out=y, workspace=wsp) for aw in ao], 5) / copies
+            res[f"B{B}"] = {"plain_us": round(t0 * 1e6, 2), "actorder_us": round(t1 * 1e6, 2),
+                            "gather_cost_us": round((t1 - t0) * 1e6, 2)}
+        out[kind] = res
+        log(f"[bench] act-order {kind} {N}x{K}: {res}")
+        del plain, ao
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) -> dict:
     """Oracle (numpy) W4A16 product on whole layers of the 70B sweep, until ~target_s of CPU time."""
     import numpy as np
@@ -460,6 +517,7 @@ def main(argv=None):
     ap.add_argument("--only-kernel", choices=["gate_up", "down", "qkv", "o"])
     ap.add_argument("--only-batch", type=int, default=0)
     ap.add_argument("--only-w8", action="store_true", help="only the W8A16 layer measurement")
+    ap.add_argument("--only-actorder", action="store_true", help="only the act-order layer measurement")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -490,6 +548,9 @@ def main(argv=None):
         return 0
     if args.only_w8:
         log(f"[bench] W8A16: {json.dumps(extras_w8(dev, None))}")
+        return 0
+    if args.only_actorder:
+        log(f"[bench] act-order: {json.dumps(extras_actorder(dev, group))}")
         return 0
 
     log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")
@@ -564,6 +625,8 @@ def main(argv=None):
         torch.cuda.empty_cache()
         int4_layer = extras.get("us_per_layer_vs_B_70b", {}).get("1", {}).get("us_per_layer")
         extras["w8a16_70b_layer"] = extras_w8(dev, int4_layer)
+        torch.cuda.empty_cache()
+        extras["actorder_70b_layer"] = extras_actorder(dev, group)
         torch.cuda.empty_cache()
 
     cpu = None

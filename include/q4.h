@@ -19,13 +19,16 @@
  *         section 7.4.1.2: INT4 codes in [-8, 7], two codes packed per byte.
  *  [CH]   "量化：PTQ、GPTQ、AWQ 与 SmoothQuant" (charles2530.github.io), section 1:
  *         4-bit symmetric range {-8, ..., 7}.
+ *  Act-order: [ARG] sections 五.3 and 十一.2 (see the act-order calls below).
+ *  Per-channel INT8 (W8A16): include/q8.h.
  *
  * Conventions common to every call
  *  - Matrices are row-major. W is [out][in] float16 (a linear layer's weight,
  *    y = x W^T); x is [B][in] float16; y is [B][out] float16.
- *  - All pointers except `stream` are DEVICE pointers owned by the caller. The
- *    library never allocates, frees or caches device memory and keeps no global
- *    state: calls are thread-safe and re-entrant.
+ *  - All pointers except `stream` are DEVICE pointers owned by the caller
+ *    (q4_actorder_perm, a host helper, is the one exception). The library never
+ *    allocates, frees or caches device memory and keeps no global state: calls
+ *    are thread-safe and re-entrant.
  *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
  *    work on it and never synchronize.
  *  - Arguments are validated on the host before any HIP call; a failed check
@@ -185,6 +188,46 @@ q4_status q4_to_canonical(const void* packed, const void* scales, const void* ze
 q4_status q4_from_canonical(const void* canon_codes, const void* canon_scales, const void* canon_zeros,
                             int32_t asym, int64_t out, int64_t in, int32_t group,
                             void* packed, void* scales, void* zeros, void* stream);
+
+/* ---- act-order (GPTQ desc_act) weights ----------------------------------------
+ * [ARG] section 五.3: channels may be quantized in descending order of the Hessian
+ * diagonal, groups of g being formed along that order, so a kernel needs a per-
+ * channel group index g_idx[k]; section 十一.2: the reorder is a gather. The library
+ * stores such weights with their input channels permuted so that every group is a
+ * contiguous run of g columns (column i of the stored matrix is channel perm[i]),
+ * and gathers the activations through perm inside the product. Scales keep the
+ * group index: scale (n, j) belongs to the channels k with g_idx[k] == j. */
+
+/* HOST function (host pointers, no HIP call): the permutation listing the channels
+ * of group 0 in ascending order, then those of group 1, ...: perm[in] from
+ * g_idx[in]. Every g_idx value must lie in [0, in/group) and every group must hold
+ * exactly `group` channels, else Q4_ERR_SHAPE (nothing is written past the checks
+ * that failed; perm's contents are then unspecified). Group rules as q4_quantize_pack. */
+q4_status q4_actorder_perm(const int32_t* g_idx, int64_t in, int32_t group, int32_t* perm);
+
+/* Symmetric INT4 quantize + pack of the column-permuted matrix W[:, perm]: as
+ * q4_quantize_pack applied to the matrix whose column i is W[:, perm[i]], so group
+ * j of the output holds channels perm[j*group .. (j+1)*group - 1]. perm: DEVICE
+ * int32 [in], 16-byte aligned, a permutation of 0..in-1 (entries outside [0, in)
+ * are clamped into the row: no out-of-bounds access, meaningless codes). */
+q4_status q4_quantize_pack_perm(const void* W, int64_t out, int64_t in, int32_t group, const int32_t* perm,
+                                void* packed, void* scales, void* stream);
+
+/* Workspace q4_gemm_perm needs: the gathered activations (B * in * 2 bytes rounded
+ * up to 256) followed by q4_workspace_bytes' split partials. */
+size_t q4_workspace_bytes_perm(int64_t B, int64_t out, int64_t in, int32_t group);
+
+/* Act-order product: y[b][n] = float16_rne( sum_j s16[n][j] * sum_{i in group j}
+ * x[b][perm[i]] * q[n][i] ), i.e. x . W_hat^T with W_hat's channels in their
+ * original order (each channel scaled by its group's scale, the g_idx gather).
+ * packed/scales as written by q4_quantize_pack_perm with the same perm (DEVICE
+ * int32 [in], 16-byte aligned). A gather kernel writes x[:, perm] into the
+ * workspace, then the GEMV (B <= 16) or skinny GEMM runs on it unchanged; the
+ * workspace is therefore always needed (q4_workspace_bytes_perm). Other arguments
+ * as q4_gemm. */
+q4_status q4_gemm_perm(const void* x, int64_t B, const void* packed, const void* scales, const int32_t* perm,
+                       int64_t out, int64_t in, int32_t group, void* y, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -197,3 +197,50 @@ def test_w8_sizes_and_validation(lib):
     assert lib.q8_gemm(FAKE, 8, FAKE, FAKE, 8192, 28672, FAKE, None, 0, None) == 6
     assert lib.q8_to_canonical(None, FAKE, 16, 128, FAKE, FAKE, None) == 1
     assert lib.q8_from_canonical(FAKE, FAKE, 16, 100, FAKE, FAKE, None) == 2
+
+
+def test_actorder_perm_host(lib):
+    """q4_actorder_perm is host logic: channels of group 0 ascending, then group 1, ..."""
+    import numpy as np
+
+    from w4a16_decode_amd import ops
+
+    r = np.random.default_rng(0)
+    for K, g in ((256, 32), (1024, 128), (512, 256)):
+        g_idx = r.permutation(np.arange(K) // g).astype(np.int32)
+        perm = ops.actorder_perm(g_idx, g)
+        assert sorted(perm.tolist()) == list(range(K))
+        for j in range(K // g):
+            blk = perm[j * g:(j + 1) * g]
+            assert np.all(g_idx[blk] == j) and np.all(np.diff(blk) > 0)
+    gi = np.zeros(64, dtype=np.int32)
+    out = np.empty(64, dtype=np.int32)
+    f = lib.q4_actorder_perm
+    assert f(None, 64, 32, out.ctypes.data) == 1
+    assert f(gi.ctypes.data, 64, 32, out.ctypes.data) == 2          # group 0 holds 64 channels
+    assert b"holds 64" in lib.q4_last_error()
+    gi2 = (np.arange(64) // 32).astype(np.int32)
+    gi2[5] = 2
+    assert f(gi2.ctypes.data, 64, 32, out.ctypes.data) == 2         # index outside [0, 2)
+    gi2[5] = -1
+    assert f(gi2.ctypes.data, 64, 32, out.ctypes.data) == 2
+    assert f(gi.ctypes.data, 64, 48, out.ctypes.data) == 3          # unsupported group
+    assert f(gi.ctypes.data, 96, 64, out.ctypes.data) == 3          # in % group != 0
+
+
+def test_actorder_validation(lib):
+    q = lib.q4_quantize_pack_perm
+    assert q(FAKE, 16, 128, 128, None, FAKE, FAKE, None) == 1
+    assert q(FAKE, 16, 128, 128, FAKE + 4, FAKE, FAKE, None) == 4    # perm misaligned
+    assert q(FAKE, 16, 96, 64, FAKE, FAKE, FAKE, None) == 3
+    g = lib.q4_gemm_perm
+    assert g(FAKE, 1, FAKE, FAKE, None, 16, 128, 128, FAKE, None, 0, None) == 1
+    assert g(FAKE, 1, FAKE, FAKE, FAKE + 8, 16, 128, 128, FAKE, None, 0, None) == 4
+    assert g(None, 0, None, None, None, 16, 128, 128, None, None, 0, None) == 0   # B = 0
+    # x is gathered into the workspace: B * in * 2 bytes rounded to 256, then the split partials
+    for B in (1, 4, 40):
+        need = lib.q4_workspace_bytes_perm(B, 64, 7168, 128)
+        x_bytes = (B * 7168 * 2 + 255) // 256 * 256
+        assert need == x_bytes + lib.q4_workspace_bytes(B, 64, 7168, 128)
+    assert g(FAKE, 40, FAKE, FAKE, FAKE, 64, 1024, 128, FAKE, None, 0, None) == 6
+    assert g(FAKE, 1, FAKE, FAKE, FAKE, 64, 1024, 128, FAKE, FAKE, 1024, None) == 6   # 2048 + partials needed

@@ -9,12 +9,15 @@ fallback: without the built library or a GPU the calls raise.
 """
 
 from .ops import (  # noqa: F401
+    ActOrderWeight,
     Q4Error,
     QuantizedWeight,
     QuantizedWeight8,
+    actorder_perm,
     from_canonical,
     gemm,
     gemm_config,
+    gemm_perm,
     groups_count,
     packed_bytes,
     q8_from_canonical,
@@ -26,10 +29,12 @@ from .ops import (  # noqa: F401
     q8_workspace_bytes,
     quantize_pack,
     quantize_pack_clip,
+    quantize_pack_perm,
     status_str,
     to_canonical,
     version,
     workspace_bytes,
+    workspace_bytes_perm,
 )
 
 __all__ = [
@@ -37,4 +42,5 @@ __all__ = [
     "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "status_str", "version",
     "QuantizedWeight8", "q8_quantize_pack", "q8_gemm", "q8_gemm_config", "q8_to_canonical", "q8_from_canonical",
     "q8_packed_bytes", "q8_workspace_bytes",
+    "ActOrderWeight", "actorder_perm", "quantize_pack_perm", "gemm_perm", "workspace_bytes_perm",
 ]

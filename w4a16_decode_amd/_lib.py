@@ -40,6 +40,10 @@ SIGNATURES = {
                                       _P]),
     "q4_to_canonical": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I32, _P, _P, _P, _P]),
     "q4_from_canonical": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I32, _P, _P, _P, _P]),
+    "q4_actorder_perm": (ctypes.c_int, [_P, _I64, _I32, _P]),
+    "q4_quantize_pack_perm": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
+    "q4_workspace_bytes_perm": (_SZ, [_I64, _I64, _I64, _I32]),
+    "q4_gemm_perm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
     "q8_packed_bytes": (_SZ, [_I64, _I64]),
     "q8_scales_count": (_SZ, [_I64]),
     "q8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -188,6 +189,9 @@ size_t splits_workspace(const q4::GemmArgs& a) {
   return a.k_splits > 1 ? (size_t)a.k_splits * a.B * a.N * sizeof(float) : 0;
 }
 
+// Act-order products gather x into the front of the workspace first.
+size_t perm_x_bytes(int64_t B, int64_t in) { return (size_t)round_up(B * in * 2, 256); }
+
 }  // namespace
 
 extern "C" {
@@ -234,14 +238,14 @@ size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group) {
 }
 
 static q4_status quantize_common(const void* W, int64_t out, int64_t in, int32_t group, void* packed, void* scales,
-                                 void* zeros, bool asym, int clip_pmin, void* stream) {
+                                 void* zeros, bool asym, int clip_pmin, void* stream, const int32_t* perm = nullptr) {
   if (!W || !packed || !scales || (asym && !zeros)) return fail(Q4_ERR_NULL, "W, packed, scales%s must be non-NULL", asym ? ", zeros" : "");
   Dims d;
   q4_status st = check_dims(out, in, group, &d);
   if (st != Q4_OK) return st;
   if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 8))
     return fail(Q4_ERR_ALIGN, "W and packed need 16-byte, scales 8-byte alignment");
-  q4::QuantArgs a{W, d.N, d.K, d.group, d.Np, d.Kp, d.Gp, asym, packed, scales, zeros, clip_pmin};
+  q4::QuantArgs a{W, d.N, d.K, d.group, d.Np, d.Kp, d.Gp, asym, packed, scales, zeros, clip_pmin, perm};
   return hip_status(q4::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
@@ -266,7 +270,7 @@ q4_status q4_quantize_pack_clip(const void* W, int64_t out, int64_t in, int32_t 
 static q4_status gemm_common(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                              bool asym, int64_t out, int64_t in, int32_t group, void* y, int rows_per_wave,
                              int waves_per_group, int k_splits, int col_tiles, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, void* stream, const int32_t* perm = nullptr) {
   if (B < 0 || B >= kMaxDim) return fail(Q4_ERR_SHAPE, "B=%lld out of range", (long long)B);
   Dims d;
   q4_status st = check_dims(out, in, group, &d);
@@ -292,6 +296,7 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
   a.Kp = d.Kp;
   a.Gp = d.Gp;
   a.y = y;
+  a.perm = perm;
   pick_shape((int)B, d, &a);
   if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0 || col_tiles > 0) {
     if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
@@ -316,11 +321,11 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
     a.waves_per_group = waves_per_group;
     a.k_splits = k_splits;
   }
-  const size_t need = splits_workspace(a);
+  const size_t need = splits_workspace(a) + (perm ? perm_x_bytes(B, in) : 0);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
-      return fail(Q4_ERR_WORKSPACE, "this shape needs %zu bytes of workspace (q4_workspace_bytes), got %zu", need,
-                  workspace ? workspace_bytes : (size_t)0);
+      return fail(Q4_ERR_WORKSPACE, "this shape needs %zu bytes of workspace (q4_workspace_bytes%s), got %zu", need,
+                  perm ? "_perm" : "", workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(Q4_ERR_ALIGN, "workspace needs 16-byte alignment");
   }
   a.workspace = workspace;
@@ -348,6 +353,57 @@ q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const voi
     return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave, waves_per_group, k_splits and col_tiles must be positive");
   return gemm_common(x, B, packed, scales, zeros, asym != 0, out, in, group, y, rows_per_wave, waves_per_group,
                      k_splits, col_tiles, workspace, workspace_bytes, stream);
+}
+
+// ---- act-order (g_idx) --------------------------------------------------------
+
+q4_status q4_actorder_perm(const int32_t* g_idx, int64_t in, int32_t group, int32_t* perm) {
+  if (!g_idx || !perm) return fail(Q4_ERR_NULL, "g_idx and perm must be non-NULL");
+  if (in <= 0 || in >= kMaxDim) return fail(Q4_ERR_SHAPE, "in=%lld must be in [1, 2^30)", (long long)in);
+  if (!group_ok(group)) return fail(Q4_ERR_GROUP, "group %d unsupported (32, 64 or a multiple of 128)", (int)group);
+  if (in % group != 0) return fail(Q4_ERR_GROUP, "in=%lld is not a multiple of group %d", (long long)in, (int)group);
+  const int64_t G = in / group;
+  std::vector<int64_t> start(G + 1, 0);  // counting sort: group sizes, then offsets
+  for (int64_t k = 0; k < in; ++k) {
+    const int64_t j = g_idx[k];
+    if (j < 0 || j >= G)
+      return fail(Q4_ERR_SHAPE, "g_idx[%lld] = %lld outside [0, %lld)", (long long)k, (long long)j, (long long)G);
+    ++start[j + 1];
+  }
+  for (int64_t j = 0; j < G; ++j) {
+    if (start[j + 1] != group)
+      return fail(Q4_ERR_SHAPE, "group %lld holds %lld channels, not %d", (long long)j, (long long)start[j + 1],
+                  (int)group);
+    start[j + 1] += start[j];
+  }
+  for (int64_t k = 0; k < in; ++k) perm[start[g_idx[k]]++] = (int32_t)k;
+  return ok();
+}
+
+q4_status q4_quantize_pack_perm(const void* W, int64_t out, int64_t in, int32_t group, const int32_t* perm,
+                                void* packed, void* scales, void* stream) {
+  if (!perm) return fail(Q4_ERR_NULL, "perm must be non-NULL");
+  if (!aligned(perm, 16)) return fail(Q4_ERR_ALIGN, "perm needs 16-byte alignment");
+  return quantize_common(W, out, in, group, packed, scales, nullptr, false, 0, stream, perm);
+}
+
+size_t q4_workspace_bytes_perm(int64_t B, int64_t out, int64_t in, int32_t group) {
+  Dims d;
+  if (B <= 0 || B >= kMaxDim || check_dims(out, in, group, &d) != Q4_OK) return 0;
+  q4::GemmArgs a{};
+  a.B = (int)B;
+  a.N = d.N;
+  pick_shape((int)B, d, &a);
+  return splits_workspace(a) + perm_x_bytes(B, in);
+}
+
+q4_status q4_gemm_perm(const void* x, int64_t B, const void* packed, const void* scales, const int32_t* perm,
+                       int64_t out, int64_t in, int32_t group, void* y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (B > 0 && !perm) return fail(Q4_ERR_NULL, "perm must be non-NULL");
+  if (perm && !aligned(perm, 16)) return fail(Q4_ERR_ALIGN, "perm needs 16-byte alignment");
+  return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, 0, 0, workspace, workspace_bytes,
+                     stream, perm);
 }
 
 q4_status q4_to_canonical(const void* packed, const void* scales, const void* zeros, int32_t asym, int64_t out,

@@ -1100,7 +1100,49 @@ hipError_t launch_mfma_r(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// x_perm[b][k] = x[b][perm[k]] (indices clamped into the row): the act-order
+// reorder of the activations ("Post-training quantization: GPTQ, AWQ and rotation",
+// arganzheng.life, section 十一.2: a gather), written to the workspace ahead of the
+// GEMV / skinny GEMM, which then run unchanged on the permuted codes. Gathering
+// inside the GEMV's activation staging instead was measured slower at every batch
+// size (2-byte gathers repeated by every workgroup; +3 to +33 us on the 70B
+// shapes against ~2.2 us for this kernel and its boundary).
+// Eight outputs per thread (K is a multiple of 32): two 16-byte loads of perm,
+// eight 2-byte gathers, one 16-byte store.
+__global__ void gather_cols_kernel(const uint16_t* __restrict__ x, int B, int K, const int32_t* __restrict__ perm,
+                                   uint16_t* __restrict__ xp) {
+  const int K8 = K / 8;
+  const int64_t total = (int64_t)B * K8;
+  const unsigned km = (unsigned)(K - 1);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = i / K8;
+    const int k = (int)(i - b * K8) * 8;
+    const int4 p0 = *reinterpret_cast<const int4*>(perm + k);
+    const int4 p1 = *reinterpret_cast<const int4*>(perm + k + 4);
+    const uint16_t* xrow = x + b * K;
+    auto at = [&](int j) __attribute__((always_inline)) { return (uint32_t)xrow[min((unsigned)j, km)]; };
+    *reinterpret_cast<uint4*>(xp + b * K + k) =
+        make_uint4(at(p0.x) | at(p0.y) << 16, at(p0.z) | at(p0.w) << 16, at(p1.x) | at(p1.y) << 16,
+                   at(p1.z) | at(p1.w) << 16);
+  }
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+  if (a.perm) {
+    // gather x into the front of the workspace, then the plain GEMV / skinny GEMM
+    // (split partials, if any, follow it at a 256-byte boundary)
+    uint16_t* xp = static_cast<uint16_t*>(a.workspace);
+    const size_t xbytes = ((size_t)a.B * a.K * 2 + 255) / 256 * 256;
+    int64_t blocks = ((int64_t)a.B * (a.K / 8) + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(gather_cols_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(a.x), a.B, a.K, a.perm, xp);
+    GemmArgs b = a;
+    b.x = xp;
+    b.perm = nullptr;
+    b.workspace = static_cast<unsigned char*>(a.workspace) + xbytes;
+    return launch_gemm(b, stream);
+  }
   if (a.B <= 16) return launch_gemv(a, stream);
   switch (a.col_tiles) {
     case 2: return launch_mfma_r<2>(a, stream);

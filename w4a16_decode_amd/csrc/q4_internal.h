@@ -16,6 +16,7 @@ struct QuantArgs {
   void* scales;
   void* zeros;
   int clip_pmin;  // > 0: symmetric clipping search over alpha = p/100, p = clip_pmin..100
+  const int32_t* perm;  // non-NULL: act-order, quantize the columns in the order perm[0..K) (symmetric)
 };
 
 struct LayoutArgs {
@@ -40,6 +41,7 @@ struct GemmArgs {
   const void* zeros;
   bool asym;
   bool q8;  // per-channel INT8 codes (B <= 16 GEMV only); group = Kp, Gp = 1
+  const int32_t* perm;  // non-NULL: act-order codes; x is read through perm (x[:, perm])
   int N, K, group;
   int Np, Kp, Gp;
   void* y;

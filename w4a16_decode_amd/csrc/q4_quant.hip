@@ -37,6 +37,35 @@ __device__ __forceinline__ Row8 load_row8(const uint16_t* __restrict__ W, int n,
   return o;
 }
 
+// Act-order columns ("Post-training quantization: GPTQ, AWQ and rotation",
+// arganzheng.life, sections 五.3 and 十一.2): the quantizer reads the matrix with
+// its columns permuted, column k of the permuted matrix being channel perm[k], so
+// every act-order group is a contiguous run of g permuted columns. Each of the 8
+// weights is a 2-byte gather from row n; indices are clamped into the row.
+__device__ __forceinline__ Row8 load_row8_perm(const uint16_t* __restrict__ W, int n, int N, int k, int K,
+                                               const int32_t* __restrict__ perm) {
+  Row8 o;
+  if (n < N && k < K) {
+    const int4 p0 = *reinterpret_cast<const int4*>(perm + k);
+    const int4 p1 = *reinterpret_cast<const int4*>(perm + k + 4);
+    const int idx[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const uint16_t* row = W + (size_t)n * K;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o.v[e] = (float)__builtin_bit_cast(_Float16, row[min((unsigned)idx[e], (unsigned)(K - 1))]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = 0.0f;
+  }
+  return o;
+}
+
+template <bool PERM>
+__device__ __forceinline__ Row8 load_w8(const uint16_t* __restrict__ W, int n, int N, int k, int K,
+                                        const int32_t* __restrict__ perm) {
+  return PERM ? load_row8_perm(W, n, N, k, K, perm) : load_row8(W, n, N, k, K);
+}
+
 __device__ __forceinline__ float wave_max4(float a) {
   // maximum over lanes l, l^16, l^32, l^48 (the four k-quarters of one row)
   a = fmaxf(a, __shfl_xor(a, 16, 64));
@@ -77,10 +106,11 @@ __device__ __forceinline__ uint32_t pack_dword(const uint32_t nib[8]) {
 }
 
 // GSUB = groups per 128-channel block (4: g = 32, 2: g = 64, 1: g = 128).
-template <int GSUB, bool ASYM>
+template <int GSUB, bool ASYM, bool PERM = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ W, int N, int K, int S,
                                                           int Gp, int64_t units, uint4* __restrict__ packed,
-                                                          uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+                                                          uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros,
+                                                          const int32_t* __restrict__ perm) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, c = lane >> 4;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -92,7 +122,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
     const int n = t * kTileRows + r;
     Row8 w[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) w[m] = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+    for (int m = 0; m < 4; ++m) w[m] = load_w8<PERM>(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
 
     uint32_t dw[4];
 #pragma unroll
@@ -224,10 +254,11 @@ __global__ __launch_bounds__(256) void quant_clip_kernel(const uint16_t* __restr
 
 // Groups of g = 128*J channels, J >= 2: one wavefront per (tile, group); the
 // group's blocks are read twice (reduction pass, then coding pass).
-template <bool ASYM>
+template <bool ASYM, bool PERM = false>
 __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restrict__ W, int N, int K, int S, int J,
                                                          int Gp, int64_t units, uint4* __restrict__ packed,
-                                                         uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+                                                         uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros,
+                                                         const int32_t* __restrict__ perm) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, c = lane >> 4;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -241,7 +272,7 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
       const int s = j * J + sb;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+        const Row8 w = load_w8<PERM>(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           a = fmaxf(a, fabsf(w.v[e]));
@@ -267,7 +298,7 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
       uint32_t dw[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+        const Row8 w = load_w8<PERM>(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
         uint32_t nib[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) nib[e] = ASYM ? asym_code(w.v[e], scale_f, zero_f) : sym_code(w.v[e], scale_f);
@@ -487,25 +518,34 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((quant_clip_kernel<1>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, a.clip_pmin, P, Sc);
     return hipGetLastError();
   }
+  const int32_t* perm = a.perm;
   if (a.group <= kSuperK) {
     const int64_t units = (int64_t)T * S;
     const int grid = grid_for(units * kWave, block);
-    if (a.group == 32) {
-      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<4, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
-      else hipLaunchKernelGGL((quant_block_kernel<4, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+    if (perm) {  // act-order: symmetric codes of the column-permuted matrix
+      if (a.group == 32)
+        hipLaunchKernelGGL((quant_block_kernel<4, false, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      else if (a.group == 64)
+        hipLaunchKernelGGL((quant_block_kernel<2, false, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      else
+        hipLaunchKernelGGL((quant_block_kernel<1, false, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+    } else if (a.group == 32) {
+      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<4, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      else hipLaunchKernelGGL((quant_block_kernel<4, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
     } else if (a.group == 64) {
-      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<2, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
-      else hipLaunchKernelGGL((quant_block_kernel<2, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<2, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      else hipLaunchKernelGGL((quant_block_kernel<2, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
     } else {
-      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<1, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
-      else hipLaunchKernelGGL((quant_block_kernel<1, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z);
+      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<1, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      else hipLaunchKernelGGL((quant_block_kernel<1, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
     }
   } else {
     const int J = a.group / kSuperK;
     const int64_t units = (int64_t)T * a.Gp;
     const int grid = grid_for(units * kWave, block);
-    if (a.asym) hipLaunchKernelGGL((quant_wide_kernel<true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z);
-    else hipLaunchKernelGGL((quant_wide_kernel<false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z);
+    if (perm) hipLaunchKernelGGL((quant_wide_kernel<false, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z, perm);
+    else if (a.asym) hipLaunchKernelGGL((quant_wide_kernel<true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z, perm);
+    else hipLaunchKernelGGL((quant_wide_kernel<false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, J, a.Gp, units, P, Sc, Z, perm);
   }
   return hipGetLastError();
 }

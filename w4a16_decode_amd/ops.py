@@ -247,6 +247,74 @@ def from_canonical(codes, scales, group: int, zeros=None) -> QuantizedWeight:
     return qw
 
 
+# ---- act-order (g_idx) weights, include/q4.h -------------------------------------
+
+
+@dataclass
+class ActOrderWeight:
+    """INT4 act-order weights: codes and scales of the column-permuted matrix, and the
+    permutation (device int32 [in]) the product gathers x through."""
+
+    qw: QuantizedWeight
+    perm: object            # int32 [in_features] on the device
+
+    @property
+    def out_features(self) -> int:
+        return self.qw.out_features
+
+    @property
+    def in_features(self) -> int:
+        return self.qw.in_features
+
+    @property
+    def group(self) -> int:
+        return self.qw.group
+
+
+def workspace_bytes_perm(batch: int, out_features: int, in_features: int, group: int) -> int:
+    return int(_lib.load().q4_workspace_bytes_perm(batch, out_features, in_features, group))
+
+
+def actorder_perm(g_idx, group: int):
+    """q4_actorder_perm (host): channels of group 0 ascending, then group 1, ...
+    g_idx: a sequence / numpy array of in_features ints. Returns a numpy int32 array."""
+    import numpy as np
+
+    gi = np.ascontiguousarray(np.asarray(g_idx), dtype=np.int32)
+    if gi.ndim != 1:
+        raise ValueError("g_idx must be 1-D")
+    perm = np.empty_like(gi)
+    _check(_lib.load().q4_actorder_perm(gi.ctypes.data, gi.size, group, perm.ctypes.data))
+    return perm
+
+
+def quantize_pack_perm(W, group: int, perm) -> ActOrderWeight:
+    """q4_quantize_pack_perm: symmetric INT4 of W[:, perm] (perm: int32 tensor on W's device)."""
+    import torch
+
+    _require_gpu(W, "W", torch.float16)
+    _require_gpu(perm, "perm", torch.int32)
+    if W.dim() != 2 or perm.shape != (W.shape[1],):
+        raise ValueError("W must be [out, in] and perm [in]")
+    out_features, in_features = W.shape
+    qw = _alloc_qw(out_features, in_features, group, False, W.device)
+    _check(_lib.load().q4_quantize_pack_perm(W.data_ptr(), out_features, in_features, group, perm.data_ptr(),
+                                             qw.packed.data_ptr(), qw.scales.data_ptr(), _stream(W)))
+    return ActOrderWeight(qw, perm)
+
+
+def gemm_perm(x, aw: ActOrderWeight, out=None, workspace=None):
+    """q4_gemm_perm: y = x . W_hat^T for act-order weights (x gathered through perm)."""
+    qw = aw.qw
+    B, out = _prep_gemm(x, qw, out)
+    lib = _lib.load()
+    need = int(lib.q4_workspace_bytes_perm(B, qw.out_features, qw.in_features, qw.group)) if B > 0 else 0
+    ws_ptr, ws_bytes = _workspace(x, need, workspace)
+    _check(lib.q4_gemm_perm(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), aw.perm.data_ptr(),
+                            qw.out_features, qw.in_features, qw.group, out.data_ptr(), ws_ptr, ws_bytes, _stream(x)))
+    return out
+
+
 # ---- per-channel INT8 weights (W8A16), include/q8.h ------------------------------
 
 
