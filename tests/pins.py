@@ -798,4 +798,67 @@ def pin_actorder_product_bruteforce(seed=44):
                 assert abs(y[b, n] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
 
 
+# --------------------------------------------- INT4 KV cache (oracle/kv.py)
+
+
+def pin_kv_bytes_per_token():
+    """[YBB] section 七: Llama-3-70B's K and V take 2 * 80 * 8 * 128 * 2 = 327,680 bytes per
+    token in BF16; INT4 with one float16 scale per 128 channels takes 2 * 80 * 8 * (64 + 2)."""
+    o = _orc()
+    assert o.kv_bytes_per_token(80, 8, 128) == 327_680
+    assert o.kv_bytes_per_token(80, 8, 128, bits=4, group=128) == 84_480
+    assert abs(327_680 / 84_480 - 3.879) < 1e-3
+
+
+def pin_kv_hand_token():
+    """One token, head_dim 16, group 8, worked by hand: group 0 has amax 7 (scale 1),
+    codes 7, -4 (tie to even), 0, 2 (tie), 2 (tie), -7, 0, 1; group 1 has amax 0.875
+    (scale 0.125), codes 1, -2, 7, 0, -7, 3, 4 (tie 3.5), 0; packed low nibble first."""
+    o = _orc()
+    K = np.zeros((1, 1, 1, 16), dtype=np.float16)
+    K[0, 0, 0, :8] = [7, -3.5, 0.5, 1.5, 2.5, -7, 0, 1]
+    K[0, 0, 0, 8:] = [0.125, -0.25, 0.875, 0.0, -0.875, 0.375, 0.4375, 0.0]
+    q, s = o.quantize_kv_int4(K, 8)
+    assert s.tolist() == [[[[1.0, 0.125]]]]
+    assert q[0, 0, 0].tolist() == [7, -4, 0, 2, 2, -7, 0, 1, 1, -2, 7, 0, -7, 3, 4, 0]
+    p = o.pack_kv_int4(q)
+    assert p.shape == (1, 1, 1, 8)
+    assert p[0, 0, 0].tolist() == [0xC7, 0x20, 0x92, 0x10, 0xE1, 0x07, 0x39, 0x04]
+    assert o.dequant_kv_int4(q, s, 8)[0, 0, 0, 8:].tolist() == [0.125, -0.25, 0.875, 0, -0.875, 0.375, 0.5, 0]
+
+
+def pin_kv_invariants(seed=51):
+    """Per group: the amax element maps to +-7, every error is within s/2, codes stay in
+    -7..7 (never -8) for random K; tokens are quantized independently (the scales follow
+    the token, as a cache appended one token at a time needs)."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    K = (r.standard_normal((2, 4, 33, 128)) * r.lognormal(size=(1, 4, 33, 1))).astype(np.float16)
+    for g in (32, 64, 128):
+        q, s = o.quantize_kv_int4(K, g)
+        assert q.min() >= -7 and q.max() <= 7
+        err = np.abs(o.dequant_kv_int4(q, s, g) - K.astype(np.float64))
+        assert np.all(err <= np.repeat(s.astype(np.float64), g, axis=-1) / 2 + 1e-12)
+        Kg = np.abs(K.reshape(2, 4, 33, 128 // g, g).astype(np.float64))
+        qg = np.abs(q.reshape(2, 4, 33, 128 // g, g))
+        hit = np.take_along_axis(qg, Kg.argmax(axis=-1)[..., None], axis=-1)
+        assert np.all(hit == 7)
+        q1, s1 = o.quantize_kv_int4(np.ascontiguousarray(K[:, :, 5:6]), g)
+        assert np.array_equal(q1, q[:, :, 5:6]) and np.array_equal(s1.view(np.uint16), s[:, :, 5:6].view(np.uint16))
+
+
+def pin_kv_attention_sink(seed=52):
+    """[YBB] section 七: attention sinks give the first tokens' K abnormally large values.
+    With scales per token and head, the other tokens' codes and scales do not change."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    K = r.standard_normal((1, 8, 64, 128)).astype(np.float16)
+    Ks = K.copy()
+    Ks[:, :, :4] *= np.float16(100)
+    q, s = o.quantize_kv_int4(K, 128)
+    qs, ss = o.quantize_kv_int4(Ks, 128)
+    assert np.array_equal(q[:, :, 4:], qs[:, :, 4:]) and np.array_equal(s[:, :, 4:], ss[:, :, 4:])
+    assert np.all(ss[:, :, :4].astype(np.float64) > 50 * s[:, :, :4].astype(np.float64))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

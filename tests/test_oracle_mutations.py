@@ -14,6 +14,7 @@ import oracle.rtn
 import oracle.clip
 import oracle.w8
 import oracle.actorder
+import oracle.kv
 from pins import ALL_PINS
 
 
@@ -309,6 +310,50 @@ def _actorder_dequant_by_position(monkeypatch):
     monkeypatch.setattr(oracle, "dequant_gidx", dq)
 
 
+def _kv_scale_per_head(monkeypatch):
+    def quant(K16, group):
+        K = np.asarray(K16)
+        b, h, sq, d = K.shape
+        amax = np.abs(K).max(axis=(2, 3), keepdims=True)                 # one scale per head, over all tokens
+        s16 = oracle.rtn.sym_scale_fp16(np.broadcast_to(amax, (b, h, sq, 1)))
+        s16 = np.repeat(s16, d // group, axis=-1)
+        with np.errstate(all="ignore"):
+            q = np.clip(np.rint(K.astype(np.float32) / np.repeat(s16, group, axis=-1).astype(np.float32)), -8, 7)
+        return np.where(np.repeat(s16, group, axis=-1) == 0, 0, q).astype(np.int8), s16
+
+    monkeypatch.setattr(oracle, "quantize_kv_int4", quant)
+
+
+def _kv_groups_strided(monkeypatch):
+    def quant(K16, group):
+        K = np.asarray(K16)
+        b, h, sq, d = K.shape
+        Kr = K.reshape(b, h, sq, group, d // group)                      # groups taken with stride d/group
+        s16 = oracle.rtn.sym_scale_fp16(np.abs(Kr).max(axis=-2))
+        with np.errstate(all="ignore"):
+            q = np.clip(np.rint(Kr.astype(np.float32) / s16.astype(np.float32)[..., None, :]), -8, 7)
+        q = np.where(s16[..., None, :] == 0, 0, q)
+        return q.astype(np.int8).reshape(b, h, sq, d), s16
+
+    monkeypatch.setattr(oracle, "quantize_kv_int4", quant)
+
+
+def _kv_pack_high_first(monkeypatch):
+    def pack(q):
+        q = np.asarray(q).astype(np.int64)
+        return (((q[..., 0::2] & 0xF) << 4) | (q[..., 1::2] & 0xF)).astype(np.uint8)
+
+    monkeypatch.setattr(oracle, "pack_kv_int4", pack)
+
+
+def _kv_bytes_no_factor_two(monkeypatch):
+    def kvb(layers, kv_heads, head_dim, bits=16, group=None, scale_bits=16):
+        per_head = head_dim * bits / 8 + ((head_dim // group) * scale_bits / 8 if group else 0)
+        return layers * kv_heads * per_head                              # K only
+
+    monkeypatch.setattr(oracle, "kv_bytes_per_token", kvb)
+
+
 MUTATIONS = [
     _scale_div8, _scale_two_alpha_over_15, _truncate, _half_away, _fp16_quotient, _nibbles_swapped,
     _device_nibble_order, _device_lane_order, _dequant_wrong_group, _gemm_rows_reversed,
@@ -317,6 +362,7 @@ MUTATIONS = [
     _w8_div128, _w8_clamp_m128, _w8_truncate, _w8_half_away, _w8_fp16_quotient, _w8_scale_per_column,
     _w8_layout_h_m_swapped, _w8_offset127, _w8_dequant_rows_shifted,
     _actorder_ascending, _actorder_gidx_inverted, _actorder_ties_reversed, _actorder_dequant_by_position,
+    _kv_scale_per_head, _kv_groups_strided, _kv_pack_high_first, _kv_bytes_no_factor_two,
 ]
 
 
