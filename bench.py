@@ -424,6 +424,31 @@ def extras_actorder(dev, group: int):
     return out
 
 
+def extras_kv(dev):
+    """INT4 KV cache (group 128 = head_dim): one Llama-3-70B layer's K (8 KV heads x 128)
+    quantized for a 32768-token prompt, and one decode step's append at B in {1, 16}."""
+    import torch
+
+    import synth
+    import w4a16_decode_amd as q4
+
+    h, d, g, S = 8, 128, 128, 32768
+    out = {}
+    src = synth.device_activation(h * S, d, seed=7, layer=0, matrix=0, device=dev).view(1, h, S, d)
+    caches = [q4.kv_cache_alloc(h, S, d, g, device=dev) for _ in range(4)]
+    t = graph_time(lambda: [q4.kv_quantize_pack(src, c, 0) for c in caches], 5) / len(caches)
+    elems = h * S * d
+    nbytes = elems * 2 + elems // 2 + (elems // g) * 2
+    out["prefill_32k_one_layer_K"] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1)}
+    for B in (1, 16):
+        tok = synth.device_activation(B * h, d, seed=8, layer=0, matrix=0, device=dev).view(B, h, 1, d)
+        cs = [q4.kv_cache_alloc(B * h, 4096, d, g, device=dev) for _ in range(8)]
+        t = graph_time(lambda: [q4.kv_quantize_pack(tok, c, 4000) for c in cs], 5) / len(cs)
+        out[f"append_B{B}_one_layer_K"] = {"us": round(t * 1e6, 2)}
+    log(f"[bench] INT4 KV cache: {out}")
+    return out
+
+
 def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) -> dict:
     """Oracle (numpy) W4A16 product on whole layers of the 70B sweep, until ~target_s of CPU time."""
     import numpy as np
@@ -518,6 +543,7 @@ def main(argv=None):
     ap.add_argument("--only-batch", type=int, default=0)
     ap.add_argument("--only-w8", action="store_true", help="only the W8A16 layer measurement")
     ap.add_argument("--only-actorder", action="store_true", help="only the act-order layer measurement")
+    ap.add_argument("--only-kv", action="store_true", help="only the INT4 KV-cache measurement")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -551,6 +577,9 @@ def main(argv=None):
         return 0
     if args.only_actorder:
         log(f"[bench] act-order: {json.dumps(extras_actorder(dev, group))}")
+        return 0
+    if args.only_kv:
+        extras_kv(dev)
         return 0
 
     log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")
@@ -627,6 +656,8 @@ def main(argv=None):
         extras["w8a16_70b_layer"] = extras_w8(dev, int4_layer)
         torch.cuda.empty_cache()
         extras["actorder_70b_layer"] = extras_actorder(dev, group)
+        torch.cuda.empty_cache()
+        extras["kv_int4_70b"] = extras_kv(dev)
         torch.cuda.empty_cache()
 
     cpu = None

@@ -244,3 +244,19 @@ def test_actorder_validation(lib):
         assert need == x_bytes + lib.q4_workspace_bytes(B, 64, 7168, 128)
     assert g(FAKE, 40, FAKE, FAKE, FAKE, 64, 1024, 128, FAKE, None, 0, None) == 6
     assert g(FAKE, 1, FAKE, FAKE, FAKE, 64, 1024, 128, FAKE, FAKE, 1024, None) == 6   # 2048 + partials needed
+
+
+def test_kv_validation(lib):
+    q = lib.q4_kv_quantize_pack
+    assert q(FAKE, 4, 1, 128, 96, FAKE, FAKE, 16, 0, None) == 3            # group
+    assert q(FAKE, 4, 1, 96, 64, FAKE, FAKE, 16, 0, None) == 3             # head_dim % group
+    assert q(FAKE, 4, 2, 128, 128, FAKE, FAKE, 16, 15, None) == 2          # pos + n > max_seq
+    assert q(FAKE, -1, 1, 128, 128, FAKE, FAKE, 16, 0, None) == 2
+    assert q(None, 0, 1, 128, 128, None, None, 16, 0, None) == 0           # nothing to do
+    assert q(None, 4, 1, 128, 128, FAKE, FAKE, 16, 0, None) == 1
+    assert q(FAKE + 4, 4, 1, 128, 128, FAKE, FAKE, 16, 0, None) == 4
+    assert q(FAKE, 4, 1, 128, 128, FAKE + 2, FAKE, 16, 0, None) == 4
+    d = lib.q4_kv_dequant
+    assert d(FAKE, FAKE, 4, 1, 128, 128, 16, 16, FAKE, None) == 2
+    assert d(FAKE, FAKE, 4, 1, 128, 128, 16, 0, FAKE + 8, None) == 4
+    assert d(None, FAKE, 4, 1, 128, 128, 16, 0, FAKE, None) == 1

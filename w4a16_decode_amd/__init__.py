@@ -3,13 +3,14 @@ W4A16 GEMV / skinny GEMM for AMD MI355X (gfx950), plus per-channel INT8
 weights with the W8A16 GEMV.
 
 Every computation runs in the HIP kernels of ``libq4.so`` behind the C ABI
-declared in ``include/q4.h`` and ``include/q8.h``; this package only marshals torch tensors
+declared in ``include/q4.h``, ``include/q8.h`` and ``include/q4_kv.h``; this package only marshals torch tensors
 (device memory, the current HIP stream) into those calls. There is no CPU
 fallback: without the built library or a GPU the calls raise.
 """
 
 from .ops import (  # noqa: F401
     ActOrderWeight,
+    KVCache4,
     Q4Error,
     QuantizedWeight,
     QuantizedWeight8,
@@ -19,6 +20,9 @@ from .ops import (  # noqa: F401
     gemm_config,
     gemm_perm,
     groups_count,
+    kv_cache_alloc,
+    kv_dequant,
+    kv_quantize_pack,
     packed_bytes,
     q8_from_canonical,
     q8_gemm,
@@ -43,4 +47,5 @@ __all__ = [
     "QuantizedWeight8", "q8_quantize_pack", "q8_gemm", "q8_gemm_config", "q8_to_canonical", "q8_from_canonical",
     "q8_packed_bytes", "q8_workspace_bytes",
     "ActOrderWeight", "actorder_perm", "quantize_pack_perm", "gemm_perm", "workspace_bytes_perm",
+    "KVCache4", "kv_cache_alloc", "kv_quantize_pack", "kv_dequant",
 ]

@@ -15,14 +15,14 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libq4.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-HEADERS = (os.path.join(INCLUDE, "q4.h"), os.path.join(INCLUDE, "q8.h"))
+HEADERS = tuple(sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")))
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 
-# name -> (restype, argtypes); mirrors include/q4.h and include/q8.h
+# name -> (restype, argtypes); mirrors the headers under include/
 SIGNATURES = {
     "q4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_error": (ctypes.c_char_p, []),
@@ -44,6 +44,8 @@ SIGNATURES = {
     "q4_quantize_pack_perm": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "q4_workspace_bytes_perm": (_SZ, [_I64, _I64, _I64, _I32]),
     "q4_gemm_perm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
+    "q4_kv_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _P, _P, _I64, _I64, _P]),
+    "q4_kv_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I64, _I64, _P, _P]),
     "q8_packed_bytes": (_SZ, [_I64, _I64]),
     "q8_scales_count": (_SZ, [_I64]),
     "q8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),

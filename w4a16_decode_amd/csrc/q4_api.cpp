@@ -14,6 +14,7 @@
 
 #include "../../include/q4.h"
 #include "../../include/q8.h"
+#include "../../include/q4_kv.h"
 #include "q4_internal.h"
 
 namespace {
@@ -582,6 +583,48 @@ q4_status q8_from_canonical(const void* canon_codes, const void* canon_scales, i
   q4::W8Args a{nullptr, d.N, d.K, d.Np, d.Kp, packed, scales, const_cast<void*>(canon_codes),
                const_cast<void*>(canon_scales)};
   return hip_status(q4::launch_w8_from_canonical(a, static_cast<hipStream_t>(stream)), "q8 from_canonical launch");
+}
+
+// ---- INT4 KV cache ---------------------------------------------------------------
+
+static q4_status check_kv(int64_t bh, int64_t n, int64_t head_dim, int32_t group, int64_t max_seq, int64_t pos) {
+  constexpr int64_t kMax31 = int64_t(1) << 31;
+  if (group != 32 && group != 64 && group != 128)
+    return fail(Q4_ERR_GROUP, "KV group %d unsupported (32, 64 or 128)", (int)group);
+  if (head_dim <= 0 || head_dim % group != 0 || head_dim >= kMax31)
+    return fail(Q4_ERR_GROUP, "head_dim=%lld must be a positive multiple of group %d", (long long)head_dim, (int)group);
+  if (bh < 0 || n < 0 || pos < 0 || max_seq <= 0 || bh >= kMax31 || n >= kMax31 || max_seq >= kMax31)
+    return fail(Q4_ERR_SHAPE, "bh=%lld, n=%lld, pos=%lld, max_seq=%lld out of range", (long long)bh, (long long)n,
+                (long long)pos, (long long)max_seq);
+  if (pos + n > max_seq)
+    return fail(Q4_ERR_SHAPE, "pos + n = %lld exceeds max_seq = %lld", (long long)(pos + n), (long long)max_seq);
+  if (bh * max_seq * head_dim >= (int64_t(1) << 46)) return fail(Q4_ERR_SHAPE, "cache too large");
+  return Q4_OK;
+}
+
+q4_status q4_kv_quantize_pack(const void* src, int64_t bh, int64_t n, int64_t head_dim, int32_t group, void* codes,
+                              void* scales, int64_t max_seq, int64_t pos, void* stream) {
+  q4_status st = check_kv(bh, n, head_dim, group, max_seq, pos);
+  if (st != Q4_OK) return st;
+  if (bh == 0 || n == 0) return ok();
+  if (!src || !codes || !scales) return fail(Q4_ERR_NULL, "src, codes, scales must be non-NULL");
+  if (!aligned(src, 16) || !aligned(codes, 4) || !aligned(scales, 2))
+    return fail(Q4_ERR_ALIGN, "src needs 16-byte, codes 4-byte, scales 2-byte alignment");
+  q4::KvArgs a{src, bh, n, (int)head_dim, group, max_seq, pos, codes, scales, nullptr};
+  return hip_status(q4::launch_kv_quantize(a, static_cast<hipStream_t>(stream)), "kv quantize launch");
+}
+
+q4_status q4_kv_dequant(const void* codes, const void* scales, int64_t bh, int64_t n, int64_t head_dim, int32_t group,
+                        int64_t max_seq, int64_t pos, void* dst, void* stream) {
+  q4_status st = check_kv(bh, n, head_dim, group, max_seq, pos);
+  if (st != Q4_OK) return st;
+  if (bh == 0 || n == 0) return ok();
+  if (!codes || !scales || !dst) return fail(Q4_ERR_NULL, "codes, scales, dst must be non-NULL");
+  if (!aligned(codes, 4) || !aligned(scales, 2) || !aligned(dst, 16))
+    return fail(Q4_ERR_ALIGN, "codes need 4-byte, scales 2-byte, dst 16-byte alignment");
+  q4::KvArgs a{nullptr, bh, n, (int)head_dim, group, max_seq, pos, const_cast<void*>(codes), const_cast<void*>(scales),
+               dst};
+  return hip_status(q4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)), "kv dequant launch");
 }
 
 }  // extern "C"

@@ -65,6 +65,20 @@ struct W8Args {
   void* canon_scales;  // float16 [N]
 };
 
+// INT4 KV cache: src [bh][n][d] float16 -> codes [bh][max_seq][d/2], scales
+// [bh][max_seq][d/group] at positions pos .. pos + n - 1 (dequant: the reverse into dst).
+struct KvArgs {
+  const void* src;
+  int64_t bh, n;
+  int d, group;
+  int64_t max_seq, pos;
+  void* codes;
+  void* scales;
+  void* dst;
+};
+
+hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t stream);
+hipError_t launch_kv_dequant(const KvArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_w8(const W8Args& a, hipStream_t stream);
 hipError_t launch_w8_to_canonical(const W8Args& a, hipStream_t stream);

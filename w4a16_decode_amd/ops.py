@@ -315,6 +315,65 @@ def gemm_perm(x, aw: ActOrderWeight, out=None, workspace=None):
     return out
 
 
+# ---- INT4 KV cache, include/q4_kv.h ------------------------------------------------
+
+
+@dataclass
+class KVCache4:
+    """INT4 KV-cache storage for bh = batch * kv_heads sequences of max_seq positions:
+    codes uint8 [bh, max_seq, head_dim / 2], scales float16 [bh, max_seq, head_dim / group]."""
+
+    codes: object
+    scales: object
+    group: int
+
+    @property
+    def head_dim(self) -> int:
+        return self.codes.shape[2] * 2
+
+    @property
+    def max_seq(self) -> int:
+        return self.codes.shape[1]
+
+
+def kv_cache_alloc(bh: int, max_seq: int, head_dim: int, group: int = 128, device="cuda") -> KVCache4:
+    import torch
+
+    if head_dim % group or group not in (32, 64, 128):
+        raise ValueError("group must be 32, 64 or 128 and divide head_dim")
+    return KVCache4(torch.zeros((bh, max_seq, head_dim // 2), dtype=torch.uint8, device=device),
+                    torch.zeros((bh, max_seq, head_dim // group), dtype=torch.float16, device=device), group)
+
+
+def kv_quantize_pack(src, cache: KVCache4, pos: int) -> None:
+    """q4_kv_quantize_pack: src float16 [batch, heads, n, head_dim] (or [bh, n, head_dim])
+    into positions pos .. pos + n - 1 of the cache."""
+    import torch
+
+    _require_gpu(src, "src", torch.float16)
+    if src.dim() == 4:
+        bh, n, d = src.shape[0] * src.shape[1], src.shape[2], src.shape[3]
+    elif src.dim() == 3:
+        bh, n, d = src.shape
+    else:
+        raise ValueError("src must be [batch, heads, n, head_dim] or [bh, n, head_dim]")
+    if bh != cache.codes.shape[0] or d != cache.head_dim:
+        raise ValueError("src does not match the cache's sequences or head_dim")
+    _check(_lib.load().q4_kv_quantize_pack(src.data_ptr(), bh, n, d, cache.group, cache.codes.data_ptr(),
+                                           cache.scales.data_ptr(), cache.max_seq, pos, _stream(src)))
+
+
+def kv_dequant(cache: KVCache4, pos: int, n: int):
+    """q4_kv_dequant: float16 [bh, n, head_dim] of positions pos .. pos + n - 1."""
+    import torch
+
+    bh = cache.codes.shape[0]
+    dst = torch.empty((bh, n, cache.head_dim), dtype=torch.float16, device=cache.codes.device)
+    _check(_lib.load().q4_kv_dequant(cache.codes.data_ptr(), cache.scales.data_ptr(), bh, n, cache.head_dim,
+                                     cache.group, cache.max_seq, pos, dst.data_ptr(), _stream(dst)))
+    return dst
+
+
 # ---- per-channel INT8 weights (W8A16), include/q8.h ------------------------------
 
 
