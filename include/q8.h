@@ -68,21 +68,22 @@ size_t q8_workspace_bytes(int64_t B, int64_t out, int64_t in);
 
 /* Fused W8A16 product ([ARG] section 二.3):
  *   y[b][n] = float16_rne( sum over 128-channel blocks of s16[n] * sum_k x[b][k] * q[n][k] )
- * float16 x and codes, float32 accumulation. The GEMV kernel runs batches of up
- * to 16 rows; a larger B is processed as consecutive slices of 16 rows, each
- * reading the weights again. x: [B][in] float16, 16-byte aligned; packed/scales
- * as written by q8_quantize_pack; y: [B][out] float16, 2-byte aligned;
- * `workspace` (16-byte aligned) must hold q8_workspace_bytes(B, out, in) bytes
- * (NULL allowed when that is 0, else Q4_ERR_WORKSPACE). Deterministic. */
+ * float16 x and codes, float32 accumulation. B <= 16 runs the GEMV kernel (one
+ * 16-column MFMA tile), a larger B the skinny MFMA GEMM (column tiles of 16 batch
+ * rows sharing each dequantized code fragment). x: [B][in] float16, 16-byte
+ * aligned; packed/scales as written by q8_quantize_pack; y: [B][out] float16,
+ * 2-byte aligned; `workspace` (16-byte aligned) must hold
+ * q8_workspace_bytes(B, out, in) bytes (NULL allowed when that is 0, else
+ * Q4_ERR_WORKSPACE). Deterministic. */
 q4_status q8_gemm(const void* x, int64_t B, const void* packed, const void* scales, int64_t out, int64_t in,
                   void* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* q8_gemm with an explicit GEMV launch shape, for tuning: `rows_per_wave` 1, 2 or
- * 4 row tiles of 16 per wavefront, `waves_per_group` 1..16 (at most 8 used with
- * rows_per_wave 4), `k_splits` workgroups splitting the channel range (at most
- * ceil(in/128); the activation slice of one split, for min(B, 16) rows, must fit
- * the device's LDS). Needs k_splits * min(B, 16) * out * 4 bytes of workspace
- * when k_splits > 1. Q4_ERR_UNSUPPORTED for shapes the kernel cannot run. */
+/* q8_gemm with an explicit GEMV launch shape (B <= 16), for tuning: `rows_per_wave`
+ * 1, 2 or 4 row tiles of 16 per wavefront, `waves_per_group` 1..16 (at most 8 used
+ * with rows_per_wave 2 or 4), `k_splits` workgroups splitting the channel range (at
+ * most ceil(in/128); the activation slice of one split must fit the device's LDS).
+ * Needs k_splits * B * out * 4 bytes of workspace when k_splits > 1.
+ * Q4_ERR_UNSUPPORTED for B > 16 and for shapes the kernel cannot run. */
 q4_status q8_gemm_config(const void* x, int64_t B, const void* packed, const void* scales, int64_t out,
                          int64_t in, void* y, int32_t rows_per_wave, int32_t waves_per_group, int32_t k_splits,
                          void* workspace, size_t workspace_bytes, void* stream);

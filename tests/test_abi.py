@@ -189,11 +189,13 @@ def test_w8_sizes_and_validation(lib):
     assert c(FAKE, 16, FAKE, FAKE, 16, 8192, FAKE, 1, 8, 1, None, 0, None) == 5  # x slice > LDS
     assert c(FAKE, 1, FAKE, FAKE, 16, 256, FAKE, 1, 1, 2, None, 0, None) == 6    # split needs workspace
     assert c(FAKE, 1, FAKE, FAKE, 16, 256, FAKE, 1, 1, 2, FAKE + 4, 128, None) == 4
-    # workspace: B = 8 over 28672 channels splits; B > 16 sizes for 16-row slices
+    # workspace: B = 8 over 28672 channels splits; few rows at B > 16 split the channels too
     ws = lib.q8_workspace_bytes(8, 8192, 28672)
     assert ws > 0 and ws % (8 * 8192 * 4) == 0
     assert lib.q8_workspace_bytes(1, 4096, 4096) == 0
-    assert lib.q8_workspace_bytes(40, 8192, 28672) == lib.q8_workspace_bytes(16, 8192, 28672)
+    # (B > 16 split counts depend on the device's LDS per workgroup: checked on the GPU)
+    assert lib.q8_workspace_bytes(40, 1024, 8192) % (40 * 1024 * 4) == 0
+    assert c(FAKE, 40, FAKE, FAKE, 16, 256, FAKE, 1, 8, 1, None, 0, None) == 5   # config is GEMV-only
     assert lib.q8_gemm(FAKE, 8, FAKE, FAKE, 8192, 28672, FAKE, None, 0, None) == 6
     assert lib.q8_to_canonical(None, FAKE, 16, 128, FAKE, FAKE, None) == 1
     assert lib.q8_from_canonical(FAKE, FAKE, 16, 100, FAKE, FAKE, None) == 2

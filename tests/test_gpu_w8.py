@@ -105,9 +105,10 @@ def test_w8_canonical_round_trip(q4):
         assert_close(y, oracle.gemm_w8_rows(x, q, s, np.arange(N)), f"imported codes N={N} K={K}")
 
 
-GEMM_CASES = [  # (B, N, K)
+GEMM_CASES = [  # (B, N, K): GEMV up to B = 16, skinny GEMM above (2, 4 and 8 column tiles, k-splits)
     (1, 1, 8), (1, 17, 96), (3, 40, 352), (2, 33, 200), (4, 48, 384), (7, 100, 1280), (8, 129, 640),
     (9, 64, 2048), (16, 200, 1024), (17, 100, 512), (40, 33, 1024), (1, 16, 8192), (2, 4000, 256), (5, 31, 8200),
+    (32, 300, 2048), (64, 129, 1000), (100, 300, 1280), (129, 40, 4096), (256, 96, 1024), (33, 1024, 8192),
 ]
 
 
@@ -185,8 +186,8 @@ def test_w8_full_70b_shapes(q4, name):
 
 
 def test_w8_full_batch_28672x8192(q4):
-    say("w8 28672x8192 B = 1, 16, 32")
-    _full_w8(q4, 28672, 8192, (1, 16, 32), seed=4, nrows=64)
+    say("w8 28672x8192 B = 1, 16, 32, 64, 256")
+    _full_w8(q4, 28672, 8192, (1, 16, 32, 64, 256), seed=4, nrows=64)
 
 
 def test_w8_full_heavy_tailed(q4):

@@ -123,10 +123,12 @@ size_t mfma_lds(int col_tiles) { return (size_t)2 * col_tiles * 16 * ((16 / col_
 // Skinny GEMM launch shapes: R x CT accumulator tiles and one partial tile per
 // group of a 128-channel block must fit the registers, the two activation tiles
 // the LDS, and every k-split must get at least one chunk of 16 / CT blocks.
-bool mfma_shape_ok(int R, int W, int KS, int CT, int group, int S) {
+bool mfma_shape_ok(int R, int W, int KS, int CT, int group, int S, bool q8 = false) {
   if (W != 4 && W != 8) return false;
   if (W == 8 && R > 2) return false;
   if (R != 1 && R != 2 && R != 4) return false;
+  // INT8 codes stage twice the bytes per block: the ring of 16 / CT blocks must fit
+  if (q8 && (R == 4 || (R == 2 && CT == 2))) return false;
   if (CT != 2 && CT != 4 && CT != 8) return false;
   const int chunks = (S + 16 / CT - 1) / (16 / CT);
   if (KS < 1 || KS > chunks) return false;
@@ -173,13 +175,13 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
   int R = 2;
   auto wgs = [&](int r) { return (int64_t)((T + 8 * r - 1) / (8 * r)) * ((col_tiles_total + CT - 1) / CT); };
   if (256 / wgs(R) > 4) R = 1;
-  while (!mfma_shape_ok(R, 8, 1, CT, d.group, S)) {
+  while (!mfma_shape_ok(R, 8, 1, CT, d.group, S, a->q8)) {
     if (R > 1) R /= 2;
     else if (CT > 2) CT /= 2;
     else break;  // unreachable: R = 1, CT = 2 always fits
   }
   int KS = (int)std::min<int64_t>(4, std::max<int64_t>(1, 256 / wgs(R)));
-  while (KS > 1 && !mfma_shape_ok(R, 8, KS, CT, d.group, S)) --KS;
+  while (KS > 1 && !mfma_shape_ok(R, 8, KS, CT, d.group, S, a->q8)) --KS;
   a->col_tiles = CT;
   a->rows_per_wave = R;
   a->waves_per_group = 8;
@@ -480,7 +482,7 @@ size_t q8_workspace_bytes(int64_t B, int64_t out, int64_t in) {
   if (B <= 0 || B >= kMaxDim || out <= 0 || in <= 0 || out >= kMaxDim || in >= kMaxDim || in % 8 != 0) return 0;
   check_w8_dims(out, in, &d);
   q4::GemmArgs a{};
-  a.B = (int)std::min<int64_t>(B, 16);
+  a.B = (int)B;
   a.N = d.N;
   a.q8 = true;
   pick_shape(a.B, d, &a);
@@ -500,8 +502,10 @@ static q4_status q8_gemm_common(const void* x, int64_t B, const void* packed, co
     return fail(Q4_ERR_ALIGN, "x and packed need 16-byte, scales and y 2-byte alignment");
   if ((int64_t)B * in >= (int64_t(1) << 40) || (int64_t)B * out >= (int64_t(1) << 40))
     return fail(Q4_ERR_SHAPE, "B*in or B*out too large");
-  const int B16 = (int)std::min<int64_t>(B, 16);
   q4::GemmArgs a{};
+  a.x = x;
+  a.B = (int)B;
+  a.y = y;
   a.packed = packed;
   a.scales = scales;
   a.q8 = true;
@@ -511,8 +515,11 @@ static q4_status q8_gemm_common(const void* x, int64_t B, const void* packed, co
   a.Np = d.Np;
   a.Kp = d.Kp;
   a.Gp = d.Gp;
-  pick_shape(B16, d, &a);
+  pick_shape((int)B, d, &a);
   if (rows_per_wave > 0 || waves_per_group > 0 || k_splits > 0) {
+    if (B > 16) return fail(Q4_ERR_UNSUPPORTED, "q8_gemm_config sets GEMV shapes (B <= 16); B=%lld runs the skinny GEMM",
+                            (long long)B);
+    const int B16 = (int)B;
     if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
       return fail(Q4_ERR_UNSUPPORTED, "rows_per_wave must be 1, 2 or 4");
     if (waves_per_group < 1 || waves_per_group > 16)
@@ -526,7 +533,6 @@ static q4_status q8_gemm_common(const void* x, int64_t B, const void* packed, co
     a.waves_per_group = waves_per_group;
     a.k_splits = k_splits;
   }
-  a.B = B16;
   const size_t need = splits_workspace(a);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
@@ -535,15 +541,7 @@ static q4_status q8_gemm_common(const void* x, int64_t B, const void* packed, co
     if (!aligned(workspace, 16)) return fail(Q4_ERR_ALIGN, "workspace needs 16-byte alignment");
   }
   a.workspace = workspace;
-  // slices of 16 batch rows, in order on the stream (they share the workspace)
-  for (int64_t b0 = 0; b0 < B; b0 += 16) {
-    a.B = (int)std::min<int64_t>(16, B - b0);
-    a.x = static_cast<const uint16_t*>(x) + b0 * in;
-    a.y = static_cast<uint16_t*>(y) + b0 * out;
-    const q4_status s2 = hip_status(q4::launch_gemm(a, static_cast<hipStream_t>(stream)), "q8 gemm launch");
-    if (s2 != Q4_OK) return s2;
-  }
-  return ok();
+  return hip_status(q4::launch_gemm(a, static_cast<hipStream_t>(stream)), "q8 gemm launch");
 }
 
 q4_status q8_gemm(const void* x, int64_t B, const void* packed, const void* scales, int64_t out, int64_t in,

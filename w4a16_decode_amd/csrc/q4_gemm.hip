@@ -870,14 +870,17 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
 // and written to the other buffer at the chunk's end, so there is one barrier per
 // chunk; codes and scales stream through a ring of NB stages (NB - 1 blocks in
 // flight) that runs on across chunk boundaries.
-template <int RT, int GSUB, bool ASYM>
+template <int RT, int GSUB, bool ASYM, int NW = 1>
 struct GStage {
-  uint4 w[RT];
+  uint4 w[RT][NW];       // NW 16-byte pieces of codes per lane and block (1: INT4, 2: INT8)
   uint2 sc[RT][GSUB];    // float16 scales of the lane's accumulator rows (C layout) per group
   uint32_t z[RT][GSUB];  // zero point of the lane's A-operand row per group (asymmetric)
 };
 
-template <int RT, int CT, int GSUB, bool ASYM, int NB, int WV>
+// Q8: per-channel INT8 codes (the GEMV's 2 KiB block layout, one scale per row
+// passed as a single group spanning the row): each code pair becomes 1024 + q + 128
+// through v_perm_b32 (magic8_i8) and one packed add of -1152 leaves q exactly.
+template <int RT, int CT, int GSUB, bool ASYM, int NB, int WV, bool Q8 = false>
 __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __restrict__ x, int B,
                                                         const uint4* __restrict__ packed,
                                                         const uint16_t* __restrict__ scales,
@@ -892,6 +895,8 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
   constexpr int C8 = KC / 8;                 // 16-byte pieces per row of a chunk
   constexpr int NT = WV * 64;                // threads
   constexpr int XCH = XROWS * C8 / NT;       // pieces of one chunk's tile per thread
+  constexpr int NW = Q8 ? 2 : 1;             // 16-byte code pieces per lane and block
+  static_assert(!Q8 || (GSUB == 1 && !ASYM), "INT8 codes are symmetric with one scale per row");
   uint16_t* xbuf = reinterpret_cast<uint16_t*>(smem);  // [2][XROWS][XSTR]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -909,12 +914,14 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
 #pragma unroll
   for (int r = 0; r < RT; ++r) tiles[r] = min(tile0 + r, T - 1);
 
-  auto load_w = [&](GStage<RT, GSUB, ASYM>& st, int s) __attribute__((always_inline)) {
+  auto load_w = [&](GStage<RT, GSUB, ASYM, NW>& st, int s) __attribute__((always_inline)) {
     s = min(c0 * NB + s, S1 - 1);  // trailing prefetches re-read the last block: no branch around loads
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const uint4* wp = packed + ((size_t)tiles[r] * S + s) * kWave + lane;
-      st.w[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp)));
+      const uint4* wp = packed + ((size_t)tiles[r] * S + s) * kWave * NW + lane;
+#pragma unroll
+      for (int h = 0; h < NW; ++h)
+        st.w[r][h] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + kWave * h)));
 #pragma unroll
       for (int gs = 0; gs < GSUB; ++gs) {
         const int j = (GSUB == 1) ? s / J : s * GSUB + gs;
@@ -954,7 +961,7 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
 
   uint4 xv[XCH];
   load_x(xv, 0);
-  GStage<RT, GSUB, ASYM> ring[NB];
+  GStage<RT, GSUB, ASYM, NW> ring[NB];
 #pragma unroll
   for (int p = 0; p < NB - 1; ++p) load_w(ring[p], p);
   store_x(xv, 0, 0);
@@ -964,7 +971,7 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
   const DequantRegs dq = DequantRegs::make();
 
   // block p of the chunk in buffer buf, codes from stage st
-  auto step = [&](const GStage<RT, GSUB, ASYM>& st, int buf, int p) __attribute__((always_inline)) {
+  auto step = [&](const GStage<RT, GSUB, ASYM, NW>& st, int buf, int p) __attribute__((always_inline)) {
     half8_t a[RT][4];
     float4_t sc[RT][GSUB];
 #pragma unroll
@@ -974,9 +981,19 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
         const _Float16 z = ASYM ? (_Float16)(float)st.z[r][gs] : (_Float16)8.0f;
         const half2_t blo = {(_Float16)-1024.0f - z, (_Float16)-1024.0f - z};
         const half2_t bhi = {(_Float16)-64.0f - z, (_Float16)-64.0f - z};
+        if constexpr (Q8) {
+          const half8_t bias8 = {(_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
+                                 (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
-        for (int mm = 0; mm < MPG; ++mm)
-          a[r][gs * MPG + mm] = dequant8r(lane_dword(st.w[r], gs * MPG + mm), dq, blo, bhi);
+          for (int mm = 0; mm < 4; ++mm) {
+            const uint4& v = st.w[r][mm >> 1];
+            a[r][mm] = magic8_i8(lane_dword(v, 2 * (mm & 1)), lane_dword(v, 2 * (mm & 1) + 1)) + bias8;
+          }
+        } else {
+#pragma unroll
+          for (int mm = 0; mm < MPG; ++mm)
+            a[r][gs * MPG + mm] = dequant8r(lane_dword(st.w[r][0], gs * MPG + mm), dq, blo, bhi);
+        }
         const half4_t sh = __builtin_bit_cast(half4_t, st.sc[r][gs]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[r][gs][i] = (float)sh[i];
@@ -1041,7 +1058,7 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
 template <int CT>
 constexpr int mfma_chunk_blocks() { return 16 / CT; }
 
-template <int RT, int CT, int GSUB, bool ASYM, int WV>
+template <int RT, int CT, int GSUB, bool ASYM, int WV, bool Q8 = false>
 hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
   constexpr int NB = mfma_chunk_blocks<CT>();
   const int T = a.Np / kTileRows;
@@ -1051,7 +1068,7 @@ hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
   const int KS = a.k_splits;
   dim3 grid((T + WV * RT - 1) / (WV * RT), (col_tiles + CT - 1) / CT, KS);
   const size_t lds = (size_t)2 * CT * 16 * (NB * kSuperK + 8) * 2;
-  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, NB, WV>), grid, dim3(WV * 64), lds, stream,
+  hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, NB, WV, Q8>), grid, dim3(WV * 64), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
                      a.Gp, J, static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
@@ -1068,13 +1085,13 @@ hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
 // Only shapes whose accumulators and per-group partial tiles fit the register file
 // (RT * CT * GSUB <= 16, and RT <= 2 with 8 wavefronts) are built; the host never
 // selects the others.
-template <int RT, int CT, int GSUB, bool ASYM>
+template <int RT, int CT, int GSUB, bool ASYM, bool Q8 = false>
 hipError_t launch_mfma_fit(const GemmArgs& a, hipStream_t stream) {
   if constexpr (RT * CT * GSUB <= 16) {
     if constexpr (RT <= 2) {  // 8 wavefronts: at most 256 VGPRs each
-      if (a.waves_per_group == 8) return launch_mfma_t<RT, CT, GSUB, ASYM, 8>(a, stream);
+      if (a.waves_per_group == 8) return launch_mfma_t<RT, CT, GSUB, ASYM, 8, Q8>(a, stream);
     }
-    return launch_mfma_t<RT, CT, GSUB, ASYM, 4>(a, stream);
+    return launch_mfma_t<RT, CT, GSUB, ASYM, 4, Q8>(a, stream);
   }
   return hipErrorInvalidConfiguration;
 }
@@ -1088,6 +1105,7 @@ hipError_t launch_mfma_g(const GemmArgs& a, hipStream_t stream) {
 
 template <int RT, int CT>
 hipError_t launch_mfma_a(const GemmArgs& a, hipStream_t stream) {
+  if (a.q8) return launch_mfma_fit<RT, CT, 1, false, true>(a, stream);
   return a.asym ? launch_mfma_g<RT, CT, true>(a, stream) : launch_mfma_g<RT, CT, false>(a, stream);
 }
 

@@ -441,9 +441,9 @@ def q8_gemm(x, qw: QuantizedWeight8, out=None, workspace=None):
 
 def q8_gemm_config(x, qw: QuantizedWeight8, rows_per_wave: int, waves_per_group: int, k_splits: int = 1, out=None,
                    workspace=None):
-    """q8_gemm_config: q8_gemm with an explicit GEMV launch shape (tuning)."""
+    """q8_gemm_config: q8_gemm with an explicit GEMV launch shape (B <= 16, tuning)."""
     B, out = _prep_gemm(x, qw, out)
-    need = 4 * k_splits * min(B, 16) * qw.out_features if k_splits > 1 else 0
+    need = 4 * k_splits * B * qw.out_features if k_splits > 1 else 0
     ws_ptr, ws_bytes = _workspace(x, need, workspace)
     _check(_lib.load().q8_gemm_config(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.out_features,
                                       qw.in_features, out.data_ptr(), rows_per_wave, waves_per_group, k_splits,
