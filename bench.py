@@ -312,7 +312,7 @@ def extras_quantize(dev):
 
 
 def extras_w8(dev, int4_us_per_layer: float | None):
-    """W8A16 (per-channel INT8) GEMV on the 70B layer's fused matrices at B in {1, 4, 8}:
+    """W8A16 (per-channel INT8) product on the 70B layer's fused matrices at B in {1, 4, 8, 64}:
     per-launch time and GB/s (copies of each matrix rotate past the 256 MB last-level
     cache), the layer total against the INT4 layer, and the INT8 quantizer's time."""
     import torch
@@ -349,7 +349,7 @@ def extras_w8(dev, int4_us_per_layer: float | None):
         kind = KIND_OF["+".join(grp)]
         res = {"shape": [N, K], "quantize_us": round(tq * 1e6, 2),
                "quantize_GBps": round((2 * N * K + perfmodel.w8_weight_bytes(N, K)) / tq / 1e9, 1)}
-        for B in (1, 4, 8):
+        for B in (1, 4, 8, 64):
             x = synth.device_activation(B, K, seed=3, layer=0, matrix=100, device=dev)
             y = torch.empty((B, N), dtype=torch.float16, device=dev)
             ws = torch.empty(max(16, q4.q8_workspace_bytes(B, N, K)), dtype=torch.uint8, device=dev)
