@@ -149,20 +149,24 @@ class Sweep:
         return sum(perfmodel.gemm_read_bytes(self.B, qw.out_features, qw.in_features, qw.group)
                    for _, _, qw, _ in self.launches())
 
-    def time_steps(self, steps: int, warmup: int) -> float:
-        """Seconds per step over `steps` graph replays (after `warmup`)."""
+    def time_steps(self, steps: int, warmup: int, per_step: list | None = None) -> float:
+        """Seconds per step over `steps` graph replays (after `warmup`). If `per_step`
+        is given, each replay's own duration (events between replays, no extra
+        synchronisation) is appended to it in seconds."""
         import torch
 
         for _ in range(warmup):
             self.graph.replay()
         torch.cuda.synchronize()
-        t0, t1 = events()
-        t0.record()
-        for _ in range(steps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        marks[0].record()
+        for i in range(steps):
             self.graph.replay()
-        t1.record()
+            marks[i + 1].record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / 1e3 / steps
+        if per_step is not None:
+            per_step.extend(marks[i].elapsed_time(marks[i + 1]) / 1e3 for i in range(steps))
+        return marks[0].elapsed_time(marks[steps]) / 1e3 / steps
 
     def time_kernel(self, pick: str, reps: int = 5):
         """Average duration of the launches named `pick` (one per layer, back to back in a
@@ -174,6 +178,22 @@ class Sweep:
         picked = [(x, qw, y) for name, x, qw, y in self.launches() if name == pick]
         t = graph_time(lambda: [q4.gemm(x, qw, out=y, workspace=self.ws) for x, qw, y in picked], reps)
         return t / len(picked), picked[0][1], len(picked) * reps
+
+
+def measured_read_gbs(dev) -> float:
+    """HBM read rate of the library's plain streaming read probe (q4_read_probe) on 8
+    rotating 256 MiB buffers of random bytes (2 GiB, past the 256 MB last-level
+    cache), timed over graph replays."""
+    import torch
+
+    import w4a16_decode_amd as q4
+
+    bufs = [torch.randint(-2**31, 2**31 - 1, (64 * 1024 * 1024,), dtype=torch.int32, device=dev) for _ in range(8)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    t = graph_time(lambda: [q4.read_probe(b, sink) for b in bufs], 5) / len(bufs)
+    nbytes = bufs[0].numel() * 4
+    del bufs
+    return nbytes / t / 1e9
 
 
 def recorded_traffic():
@@ -465,24 +485,35 @@ def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) 
     except Exception:
         threads = 1
     order = {name: i for i, name in enumerate(synth.MATRIX_ORDER)}
-    total_bytes, t_total, layers = 0, 0.0, 0
+    total_bytes, t_total, t_deq, t_mm, layers = 0, 0.0, 0.0, 0.0, 0
+    t_q, q_bytes = 0.0, 0
     while t_total < target_s and layers < max_layers:
-        for grp in synth.FUSED_GROUPS:
+        for gi, grp in enumerate(synth.FUSED_GROUPS):
             parts = [synth.device_weight(*synth.LLAMA3_70B[n], seed=3, layer=layers, matrix=order[n], device=dev)
                      for n in grp]
             W = (torch.cat(parts, 0) if len(parts) > 1 else parts[0]).cpu().numpy()
             del parts
             N, K = W.shape
             x = synth.activation(1, K, seed=11, layer=layers)
-            q, s = oracle.quantize_sym(W, group)  # setup, not timed
+            t0 = time.perf_counter()
+            q, s = oracle.quantize_sym(W, group)  # timed on the first layer's q/k/v only
+            if layers == 0 and gi == 0:
+                t_q = time.perf_counter() - t0
+                q_bytes = perfmodel.quantize_bytes(N, K, group)
             del W
             t0 = time.perf_counter()
-            yy = oracle.gemm_ref(x, oracle.dequant_sym(q, s, group))
-            t_total += time.perf_counter() - t0
+            wh = oracle.dequant_sym(q, s, group)
+            t1 = time.perf_counter()
+            yy = oracle.gemm_ref(x, wh)
+            t2 = time.perf_counter()
+            t_deq += t1 - t0
+            t_mm += t2 - t1
+            t_total += t2 - t0
             assert yy.shape == (1, N) and np.all(np.isfinite(yy))
             total_bytes += perfmodel.gemm_read_bytes(1, N, K, group)
         layers += 1
-    return {"seconds": t_total, "bytes": total_bytes, "threads": threads, "layers": layers}
+    return {"seconds": t_total, "bytes": total_bytes, "threads": threads, "layers": layers,
+            "dequant_s": t_deq, "matmul_s": t_mm, "quantize_s": t_q, "quantize_bytes": q_bytes}
 
 
 def only_kernel(kind: str, reps: int, layers: int, dev, group: int):
@@ -534,8 +565,8 @@ def copy_calibration(dev):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=80)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -590,7 +621,9 @@ def main(argv=None):
 
     sweep = Sweep(model, 1, seed=3, device=dev)
     sweep.capture()
-    step_s = sweep.time_steps(args.steps, args.warmup)
+    per_step = []
+    step_s = sweep.time_steps(args.steps, args.warmup, per_step)
+    pct = np.percentile(np.array(per_step) * 1e3, [10, 50, 90])
     bytes_step = sweep.bytes_per_step()
     gbs = bytes_step / step_s / 1e9
     log(f"[bench] B=1 sweep: {step_s * 1e3:.3f} ms/step, {gbs:.1f} GB/s ({gbs / perfmodel.HBM_PEAK_GBS:.1%} of 8 TB/s)")
@@ -601,9 +634,12 @@ def main(argv=None):
     k_gbs = kbytes / d_avg / 1e9
     log(f"[bench] gate/up GEMV {qw0.out_features}x{qw0.in_features}: {d_avg * 1e6:.2f} us, {k_gbs:.1f} GB/s")
     traffic = recorded_traffic()
+    read_gbs = measured_read_gbs(dev)
+    log(f"[bench] read probe: {read_gbs:.1f} GB/s; gate/up at {k_gbs / read_gbs:.1%} of it")
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / perfmodel.HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
+                "measured_read_GBps": round(read_gbs, 1), "frac_of_measured_read": round(k_gbs / read_gbs, 4),
                 "kernel": f"gemv_kernel, fused gate/up {qw0.out_features}x{qw0.in_features}, B=1, g=128",
                 "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes, "launches_timed": n_timed}
 
@@ -666,7 +702,12 @@ def main(argv=None):
         cpu_gbs = res["bytes"] / res["seconds"] / 1e9
         cpu = {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": res["threads"], "kind": "oracle",
                "sample": f"the first {res['layers']} layers of the 70B sweep (q/k/v, o, gate/up, down), B=1: "
-                         f"float64 dequantize + numpy matmul, {res['seconds']:.1f} s of oracle time"}
+                         f"float64 dequantize + numpy matmul, {res['seconds']:.1f} s of oracle time",
+               "stages": {"dequant_s": round(res["dequant_s"], 2), "dequant_cores": 1,
+                          "matmul_s": round(res["matmul_s"], 2), "matmul_cores": res["threads"],
+                          "quantize_GBps": round(res["quantize_bytes"] / res["quantize_s"] / 1e9, 3),
+                          "quantize_sample": "layer 0's fused q/k/v (10240x8192), numpy on 1 core",
+                          "host_cpus": os.cpu_count()}}
         log(f"[bench] cpu oracle: {cpu_gbs:.3f} GB/s over {res['seconds']:.1f}s ({res['layers']} layers)")
 
     out = {
@@ -677,6 +718,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step_p10_p50_p90": [round(float(v), 4) for v in pct],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -189,6 +189,14 @@ q4_status q4_from_canonical(const void* canon_codes, const void* canon_scales, c
                             int32_t asym, int64_t out, int64_t in, int32_t group,
                             void* packed, void* scales, void* zeros, void* stream);
 
+/* Measurement helper: read `bytes` (a positive multiple of 8192) from the device
+ * buffer `buf` (16-byte aligned) with a plain streaming read kernel, one workgroup
+ * per CU, so the GEMV's bytes / time can be compared with the read rate the same
+ * device sustains ([YBB] section 一: decode is bound by the bytes it reads). `sink`
+ * is a device uint32 the kernel writes only in a case random data never produces.
+ * Returns Q4_ERR_SHAPE for other sizes, Q4_ERR_NULL / Q4_ERR_ALIGN as usual. */
+q4_status q4_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
 /* ---- act-order (GPTQ desc_act) weights ----------------------------------------
  * [ARG] section 五.3: channels may be quantized in descending order of the Hessian
  * diagonal, groups of g being formed along that order, so a kernel needs a per-

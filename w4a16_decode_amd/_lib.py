@@ -44,6 +44,7 @@ SIGNATURES = {
     "q4_quantize_pack_perm": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "q4_workspace_bytes_perm": (_SZ, [_I64, _I64, _I64, _I32]),
     "q4_gemm_perm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
+    "q4_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "q4_kv_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _P, _P, _I64, _I64, _P]),
     "q4_kv_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I64, _I64, _P, _P]),
     "q8_packed_bytes": (_SZ, [_I64, _I64]),

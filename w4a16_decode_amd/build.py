@@ -22,7 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libq4.so")
-SOURCES = ["q4_api.cpp", "q4_quant.hip", "q4_gemm.hip", "q4_kv.hip"]
+SOURCES = ["q4_api.cpp", "q4_quant.hip", "q4_gemm.hip", "q4_kv.hip", "q4_probe.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_*_f32 (float2 arithmetic is issued as scalar VALU ops).

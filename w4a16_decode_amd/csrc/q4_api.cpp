@@ -93,6 +93,21 @@ size_t lds_per_block() {
   return lim;
 }
 
+// Compute units of the current device (256 if it cannot be queried).
+int device_cu_count() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
+  cache[dev] = v;
+  return v;
+}
+
 // LDS of one GEMV workgroup with a single unit of work (q4_gemm.hip, GemvLds): x
 // slice + zero row, the per-unit biases of symmetric codes, the partial sums of
 // one unit and the unit counter. The launch fits as many units as the limit holds.
@@ -623,6 +638,16 @@ q4_status q4_kv_dequant(const void* codes, const void* scales, int64_t bh, int64
   q4::KvArgs a{nullptr, bh, n, (int)head_dim, group, max_seq, pos, const_cast<void*>(codes), const_cast<void*>(scales),
                dst};
   return hip_status(q4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)), "kv dequant launch");
+}
+
+// ---- read probe ----------------------------------------------------------------
+
+q4_status q4_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink) return fail(Q4_ERR_NULL, "buf and sink must be non-NULL");
+  if (bytes == 0 || bytes % 8192 != 0) return fail(Q4_ERR_SHAPE, "bytes=%zu must be a positive multiple of 8192", bytes);
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(Q4_ERR_ALIGN, "buf needs 16-byte, sink 4-byte alignment");
+  return hip_status(q4::launch_read_probe(buf, (int64_t)(bytes / 8192), sink, device_cu_count(),
+                                          static_cast<hipStream_t>(stream)), "read probe launch");
 }
 
 }  // extern "C"

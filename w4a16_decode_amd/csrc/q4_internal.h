@@ -78,6 +78,8 @@ struct KvArgs {
 };
 
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t stream);
+// Read `pieces` x 8 KiB from buf with one workgroup of 8 wavefronts per CU.
+hipError_t launch_read_probe(const void* buf, int64_t pieces, void* sink, int cus, hipStream_t stream);
 hipError_t launch_kv_dequant(const KvArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_w8(const W8Args& a, hipStream_t stream);

@@ -1,0 +1,42 @@
+// Plain HBM read probe: the read rate the GEMV's byte count is measured against.
+//
+// The decode GEMV is bound by the bytes of weights it reads ("LLM 后训练量化深度实战…",
+// www.ybb.press, section 一), so besides the datasheet peak its achieved GB/s is
+// compared with what a kernel that only reads can get on the same device. Each
+// wavefront reads 8 KiB pieces (8 loads of 16 bytes per lane issued together, then
+// consumed), pieces assigned round-robin over all wavefronts; the data is folded
+// into an XOR that is stored only if it equals a constant no input produces in
+// practice, so no load is dead.
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+__global__ __launch_bounds__(512) void read_probe_kernel(const uint4* __restrict__ buf, int64_t pieces,
+                                                         uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  uint32_t acc = 0;
+  for (int64_t p = wave; p < pieces; p += nwaves) {
+    const uint4* base = buf + p * 512 + lane;  // 8 KiB = 512 x 16 bytes per piece
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + 64 * u)));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* buf, int64_t pieces, void* sink, int cus, hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(cus), dim3(512), 0, stream, static_cast<const uint4*>(buf), pieces,
+                     static_cast<uint32_t*>(sink));
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -271,6 +271,13 @@ class ActOrderWeight:
         return self.qw.group
 
 
+def read_probe(buf, sink) -> None:
+    """q4_read_probe: read all of `buf` (a contiguous device tensor of a multiple of 8 KiB)
+    with the plain streaming read kernel; `sink` is a device int32 tensor."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.load().q4_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)))
+
+
 def workspace_bytes_perm(batch: int, out_features: int, in_features: int, group: int) -> int:
     return int(_lib.load().q4_workspace_bytes_perm(batch, out_features, in_features, group))
 
