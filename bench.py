@@ -580,8 +580,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build has no "
-              "multi-GPU path (the GEMV would shard by output rows, see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library has no "
+              "multi-GPU path (the GEMV would shard by output rows)", file=sys.stderr)
         return 2
 
     import numpy as np

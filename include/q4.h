@@ -73,7 +73,7 @@ typedef enum {
   Q4_ERR_SHAPE = 2,       /* out/in/B out of range or overflowing                        */
   Q4_ERR_GROUP = 3,       /* group unsupported, or in % group != 0 ([YBB] section 二)    */
   Q4_ERR_ALIGN = 4,       /* a pointer is not aligned as the call requires               */
-  Q4_ERR_UNSUPPORTED = 5, /* a valid request this build does not handle (e.g. config)    */
+  Q4_ERR_UNSUPPORTED = 5, /* a valid request the library does not handle (e.g. config)    */
   Q4_ERR_WORKSPACE = 6,   /* workspace smaller than q4_workspace_bytes() asks for        */
   Q4_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                  */
 } q4_status;

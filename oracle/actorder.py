@@ -22,7 +22,7 @@ kernel-visible path):
   4. w_hat[n, k] = s16[n, g_idx[k]] * q[n, k] (the per-channel scale gather), and
      y = x . w_hat^T.
 
-Readings (listed in DESIGN.md):
+Readings (where the pages are silent, ambiguous or disagree):
   A1 Ties in h keep ascending channel order (a stable sort of -h).
   A2 Groups are consecutive runs of g channels in quantization order; in % g == 0.
   A3 Inside a group the codes and the scale are plain RTN: act-order changes which

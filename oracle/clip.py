@@ -20,7 +20,7 @@ Steps, per group of g consecutive input channels of a row:
      smaller clip), so p_min = 100 -- and any group where clipping does not pay --
      is exactly RTN.
 
-Readings (listed in DESIGN.md):
+Readings (where the pages are silent, ambiguous or disagree):
   C1 The error is the weight reconstruction error of the group itself (the pages
      search "on calibration data"; weight-only RTN has none, and the squared
      weight error is the quantity section 三.2's formula writes out).

@@ -10,7 +10,7 @@ two INT4 codes are packed per byte (pack_int4, which the page leaves undefined).
 2 * 80 * 8 * 128 * 2 = 327,680 bytes per token in BF16; scales must follow the
 tokens they belong to (one per token and head at group_size = head_dim).
 
-Readings (listed in DESIGN.md):
+Readings (where the pages are silent, ambiguous or disagree):
   K1 The rounding is that of the weight quantizer (readings R1-R4 of rtn.py): a
      float16 scale fp16(fp32(amax) / 7), the IEEE float32 quotient, round half to
      even, codes 0 where the scale is 0.

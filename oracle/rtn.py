@@ -14,7 +14,7 @@ Formulas followed:
     [ARG section 二.2, integer-side zero point; WIKI section 7.4.1.1 with
      2^b - 1 = 15 for b = 4]
 
-Readings (the pages are silent or disagree; each is listed in the design doc):
+Readings (where the pages are silent or disagree):
   R1 The quotient divides by the *stored* float16 scale: the page's code
      quantizes and dequantizes with the same ``scale`` tensor, which is float16
      because W is.

@@ -11,7 +11,7 @@ Formulas followed:
   * the product keeps 16-bit activations and multiplies them with the
     dequantized weights, y = x . w_hat^T [ARG section 二.3].
 
-Readings (listed in DESIGN.md):
+Readings (where the pages are silent, ambiguous or disagree):
   W1 Scale bits: s16 = float16_rne(float32(amax) / 127.0f), the rounding of a
      float16 tensor division (as R2 for INT4). The quick code example clamps
      amax at 1e-6 first; that changes no float16 scale (any amax below 1e-6
