@@ -24,7 +24,8 @@ The same line carries:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 Profiling helpers: --only-kernel {gate_up,down,qkv,o} [--reps N] runs just that
 GEMV kind of a few 70B layers; --only-batch B [--reps N] runs the product on one
-28672x8192 matrix at batch B; --copy-calibration runs a 256 MiB device copy.
+28672x8192 matrix at batch B; --only-quantize, --only-w8, --only-actorder, --only-kv
+run just that extra measurement; --copy-calibration runs a 256 MiB device copy.
 """
 
 from __future__ import annotations
@@ -575,6 +576,7 @@ def main(argv=None):
     ap.add_argument("--only-w8", action="store_true", help="only the W8A16 layer measurement")
     ap.add_argument("--only-actorder", action="store_true", help="only the act-order layer measurement")
     ap.add_argument("--only-kv", action="store_true", help="only the INT4 KV-cache measurement")
+    ap.add_argument("--only-quantize", action="store_true", help="only the heavy-tailed quantizer measurement")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -611,6 +613,9 @@ def main(argv=None):
         return 0
     if args.only_kv:
         extras_kv(dev)
+        return 0
+    if args.only_quantize:
+        log(f"[bench] quantize: {json.dumps(extras_quantize(dev))}")
         return 0
 
     log(f"[bench] {q4.version()} on {torch.cuda.get_device_name(0)}")

@@ -1,0 +1,97 @@
+"""The quantize kernels' division-free code decision, modelled in numpy float32.
+
+The kernels round w / s half to even (float16 w and s) from r = fl(1 / s) and
+t = fl(w * r): where t lies within 2^-14 of h = floor(t) + 1/2 the code is rint(h),
+else rint(t). These tests check that this decision equals the rounding of the IEEE
+float32 quotient that the pages' formula q = round(w / scale) is taken as ("LLM
+后训练量化深度实战…", www.ybb.press, section 二), for every finite float16 w against a
+spread of float16 scales, every exact tie, and the range limit |w / s| < 512, in
+both evaluation orders of t - h (rounded product, or fused multiply-add).
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+BAND = np.float32(2.0 ** -14)
+
+
+def _all_finite_fp16():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    return v[np.isfinite(v)]
+
+
+def _scales(n_random=160, seed=5):
+    rng = np.random.default_rng(seed)
+    pos = _all_finite_fp16()
+    pos = pos[pos > 0]
+    picks = rng.choice(pos, size=n_random, replace=False)
+    special = np.array([2.0 ** -24, 3 * 2.0 ** -24, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -24, 1.0, 3.0, 7.0,
+                        0.02 / 7, 1 / 7, 2047 / 1024, 65504.0, 1e-3, 5e-5], dtype=np.float16)
+    return np.unique(np.concatenate([picks, special]))
+
+
+def _model(w32, s32, fused):
+    """The kernels' arithmetic in float32 (fused: t - h from the exact product w * r)."""
+    r = np.float32(1.0) / s32
+    t = w32 * r
+    h = np.floor(t) + np.float32(0.5)
+    if fused:
+        d = (w32.astype(np.float64) * np.float64(r) - h.astype(np.float64)).astype(np.float32)
+    else:
+        d = t - h
+    return np.rint(np.where(np.abs(d) < BAND, h, t))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_decision_equals_ieee_quotient_all_fp16(fused):
+    w = _all_finite_fp16().astype(np.float32)
+    for s16 in _scales():
+        s32 = np.float32(s16)
+        ref = np.rint(w / s32)
+        got = _model(w, s32, fused)
+        inside = np.abs(ref) < 511
+        bad = inside & (got != ref)
+        assert not bad.any(), (float(s16), w[bad][:4])
+        # past the range the decision may differ by one but stays beyond every clamp bound
+        assert np.all(np.abs(got[~inside]) >= 510)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_exact_ties_round_to_even(fused):
+    checked = 0
+    for s16 in _scales():
+        s = Fraction(float(s16))
+        for k in range(-130, 130):
+            w_exact = (Fraction(2 * k + 1, 2)) * s
+            w16 = np.float16(float(w_exact))
+            if not np.isfinite(w16) or Fraction(float(w16)) != w_exact:
+                continue  # not a float16 value
+            got = _model(np.array([w16], dtype=np.float32), np.float32(s16), fused)[0]
+            even = k if k % 2 == 0 else k + 1
+            assert got == even, (float(s16), float(w16))
+            checked += 1
+    assert checked > 1000
+
+
+def test_non_ties_keep_the_gap():
+    # the margin the decision relies on: a quotient that is not a half-integer
+    # stays at least 2^-12 away from every half-integer (1/(2 m_s) >= 1/4094 when
+    # w's exponent reaches s's minus 1; 1/2 - 2^-12 at most below that)
+    w = _all_finite_fp16().astype(np.float64)
+    w = w[(w > 0) & (w < 2048)]
+    for s16 in _scales(40, seed=9):
+        q = w / float(s16)
+        q = q[q < 600]
+        dist = np.abs(q - (np.floor(q) + 0.5))
+        assert np.all((dist == 0) | (dist >= 2.0 ** -12)), float(s16)
+
+
+def test_zero_scale_gives_code_zero():
+    # the kernels use r = 0 for s == 0: every weight gets q = 0
+    w = _all_finite_fp16().astype(np.float32)
+    t = w * np.float32(0.0)
+    h = np.floor(t) + np.float32(0.5)
+    assert np.all(np.rint(np.where(np.abs(t - h) < BAND, h, t)) == 0)

@@ -14,9 +14,11 @@
 // Mapping: one lane per 8 channels of a token (16-byte load, 4-byte store); the
 // GL = group / 8 lanes of a group are consecutive and aligned in the wavefront, so
 // the group amax is a butterfly over GL lanes. Rounding as the weight quantizer:
-// float16 scale fp16(fp32(amax) / 7), IEEE float32 quotient, round half to even.
+// float16 scale fp16(fp32(amax) / 7), the quotient rounded half to even (the IEEE
+// float32 quotient's decision, taken without a per-element divide: q4_rtn.h).
 #include "q4_device.h"
 #include "q4_internal.h"
+#include "q4_rtn.h"
 
 namespace q4 {
 namespace {
@@ -46,11 +48,11 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
 #pragma unroll
     for (int m = 1; m < GL; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
     const _Float16 s16 = (_Float16)(fmaxf(a, 1e-12f) / 7.0f);
-    const float sf = (float)s16;
+    const float rcp = rtn_recip((float)s16);  // 0 for a zero scale: codes 0
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int q = sf == 0.0f ? 0 : (int)fminf(fmaxf(rintf(v[e] / sf), -8.0f), 7.0f);
+      const int q = (int)fminf(fmaxf(rtn_quot(v[e], rcp), -8.0f), 7.0f);
       word |= (uint32_t)(q & 0xF) << (4 * e);
     }
     if (valid) {

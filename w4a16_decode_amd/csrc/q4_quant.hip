@@ -10,11 +10,13 @@
 // channels 32*m + 8*c .. +7 (16 bytes), which are exactly the 32 codes it will
 // store as its 16-byte slice of the block. A group of 128 channels of a row is
 // spread over the four lanes r, r+16, r+32, r+48; its amax is reduced across
-// them with two cross-lane exchanges. The quotient is an IEEE float32 division
-// rounded half-to-even (v_rndne_f32): dividing two float16 values this way makes
-// the same decision as the exact rational quotient.
+// them with two cross-lane exchanges. Codes round the quotient w / s half to even,
+// which for float16 w and s is the decision of the exact rational quotient (and of
+// the IEEE float32 one); it is taken from one reciprocal per scale and a multiply
+// per weight (q4_rtn.h).
 #include "q4_device.h"
 #include "q4_internal.h"
+#include "q4_rtn.h"
 
 namespace q4 {
 namespace {
@@ -83,18 +85,15 @@ __device__ __forceinline__ uint16_t half_bits(_Float16 h) { return __builtin_bit
 // Symmetric scale of a group from its amax (float32 IEEE divide, RNE to float16).
 __device__ __forceinline__ _Float16 sym_scale(float amax) { return (_Float16)(fmaxf(amax, 1e-12f) / 7.0f); }
 
-__device__ __forceinline__ uint32_t sym_code(float w, float s) {
-  // offset-binary nibble q + 8, q = clamp(rint(w / s), -8, 7); 0 code for s == 0
-  if (s == 0.0f) return 8u;
-  float q = rintf(w / s);
-  q = fminf(fmaxf(q, -8.0f), 7.0f);
+// r = rtn_recip(s): 0 for s == 0, which gives the code of q = 0 (and z = 0)
+__device__ __forceinline__ uint32_t sym_code(float w, float r) {
+  // offset-binary nibble q + 8, q = clamp(rint(w / s), -8, 7)
+  const float q = fminf(fmaxf(rtn_quot(w, r), -8.0f), 7.0f);
   return (uint32_t)((int)q + 8);
 }
 
-__device__ __forceinline__ uint32_t asym_code(float w, float s, float z) {
-  if (s == 0.0f) return 0u;
-  float q = rintf(w / s) + z;
-  q = fminf(fmaxf(q, 0.0f), 15.0f);
+__device__ __forceinline__ uint32_t asym_code(float w, float r, float z) {
+  const float q = fminf(fmaxf(rtn_quot(w, r) + z, 0.0f), 15.0f);
   return (uint32_t)q;
 }
 
@@ -154,12 +153,13 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
         scale_f = (float)s16;
         if (scale_f != 0.0f) zero_f = fminf(fmaxf(rintf(-lo / scale_f), 0.0f), 15.0f);
       }
+      const float rcp = rtn_recip(scale_f);
 #pragma unroll
       for (int m = gs * MPG; m < (gs + 1) * MPG; ++m) {
         uint32_t nib[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          nib[e] = ASYM ? asym_code(w[m].v[e], scale_f, zero_f) : sym_code(w[m].v[e], scale_f);
+          nib[e] = ASYM ? asym_code(w[m].v[e], rcp, zero_f) : sym_code(w[m].v[e], rcp);
         dw[m] = pack_dword(nib);
       }
       if (c == 0) {
@@ -188,9 +188,8 @@ __device__ __forceinline__ double wave_sum4(double a) {
   return a;
 }
 
-__device__ __forceinline__ float clip_q(float w, float s) {
-  return s == 0.0f ? 0.0f : fminf(fmaxf(rintf(w / s), -7.0f), 7.0f);
-}
+// clamp(rint(w / s), -7, 7) with r = rtn_recip(s) (0 for s == 0)
+__device__ __forceinline__ float clip_q(float w, float r) { return fminf(fmaxf(rtn_quot(w, r), -7.0f), 7.0f); }
 
 template <int GSUB>
 __global__ __launch_bounds__(256) void quant_clip_kernel(const uint16_t* __restrict__ W, int N, int K, int S, int Gp,
@@ -224,12 +223,13 @@ __global__ __launch_bounds__(256) void quant_clip_kernel(const uint16_t* __restr
         const float alpha = (float)p / 100.0f;
         const _Float16 sp = (_Float16)(fmaxf(a * alpha, 1e-12f) / 7.0f);
         const float sf = (float)sp;
+        const float rp = rtn_recip(sf);
         double err = 0.0;
 #pragma unroll
         for (int m = gs * MPG; m < (gs + 1) * MPG; ++m)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const double d = (double)(sf * clip_q(w[m].v[e], sf) - w[m].v[e]);
+            const double d = (double)(sf * clip_q(w[m].v[e], rp) - w[m].v[e]);
             err = __builtin_fma(d, d, err);
           }
         err = wave_sum4(err);
@@ -238,12 +238,12 @@ __global__ __launch_bounds__(256) void quant_clip_kernel(const uint16_t* __restr
           s16 = sp;
         }
       }
-      const float scale_f = (float)s16;
+      const float rcp = rtn_recip((float)s16);
 #pragma unroll
       for (int m = gs * MPG; m < (gs + 1) * MPG; ++m) {
         uint32_t nib[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) nib[e] = (uint32_t)((int)clip_q(w[m].v[e], scale_f) + 8);
+        for (int e = 0; e < 8; ++e) nib[e] = (uint32_t)((int)clip_q(w[m].v[e], rcp) + 8);
         dw[m] = pack_dword(nib);
       }
       if (c == 0) scales[((size_t)t * Gp + (size_t)s * GSUB + gs) * kTileRows + r] = half_bits(s16);
@@ -293,6 +293,7 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
       scale_f = (float)s16;
       if (scale_f != 0.0f) zero_f = fminf(fmaxf(rintf(-lo / scale_f), 0.0f), 15.0f);
     }
+    const float rcp = rtn_recip(scale_f);
     for (int sb = 0; sb < J; ++sb) {
       const int s = j * J + sb;
       uint32_t dw[4];
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
         const Row8 w = load_w8<PERM>(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
         uint32_t nib[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) nib[e] = ASYM ? asym_code(w.v[e], scale_f, zero_f) : sym_code(w.v[e], scale_f);
+        for (int e = 0; e < 8; ++e) nib[e] = ASYM ? asym_code(w.v[e], rcp, zero_f) : sym_code(w.v[e], rcp);
         dw[m] = pack_dword(nib);
       }
       packed[((size_t)t * S + s) * kWave + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
@@ -347,10 +348,10 @@ __global__ __launch_bounds__(256) void w8_scale_kernel(const uint16_t* __restric
   }
 }
 
-__device__ __forceinline__ uint32_t w8_code(float w, float s) {
-  // offset-binary byte q + 128, q = clamp(rint(w / s), -127, 127); code 0 for s == 0
-  if (s == 0.0f) return 128u;
-  const float q = fminf(fmaxf(rintf(w / s), -127.0f), 127.0f);
+__device__ __forceinline__ uint32_t w8_code(float w, float r) {
+  // offset-binary byte q + 128, q = clamp(rint(w / s), -127, 127), r = rtn_recip(s)
+  // (code 0 for s == 0)
+  const float q = fminf(fmaxf(rtn_quot(w, r), -127.0f), 127.0f);
   return (uint32_t)((int)q + 128);
 }
 
@@ -364,15 +365,15 @@ __global__ __launch_bounds__(256) void w8_pack_kernel(const uint16_t* __restrict
   for (int64_t u = wave; u < units; u += nwaves) {
     const int t = (int)(u / S), s = (int)(u % S);
     const int n = t * kTileRows + r;
-    const float sf = (float)__builtin_bit_cast(_Float16, scales[n]);
+    const float rcp = rtn_recip((float)__builtin_bit_cast(_Float16, scales[n]));
     uint32_t d[8];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        d[2 * m + i] = w8_code(w.v[4 * i], sf) | (w8_code(w.v[4 * i + 1], sf) << 8) |
-                       (w8_code(w.v[4 * i + 2], sf) << 16) | (w8_code(w.v[4 * i + 3], sf) << 24);
+        d[2 * m + i] = w8_code(w.v[4 * i], rcp) | (w8_code(w.v[4 * i + 1], rcp) << 8) |
+                       (w8_code(w.v[4 * i + 2], rcp) << 16) | (w8_code(w.v[4 * i + 3], rcp) << 24);
     }
     uint4* out = packed + ((size_t)t * S + s) * 2 * kWave + lane;
     out[0] = make_uint4(d[0], d[1], d[2], d[3]);
