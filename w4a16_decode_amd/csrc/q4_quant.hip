@@ -14,6 +14,10 @@
 // which for float16 w and s is the decision of the exact rational quotient (and of
 // the IEEE float32 one); it is taken from one reciprocal per scale and a multiply
 // per weight (q4_rtn.h).
+#include <algorithm>
+#include <map>
+#include <mutex>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 #include "q4_rtn.h"
@@ -25,18 +29,21 @@ struct Row8 {
   float v[8];
 };
 
-__device__ __forceinline__ Row8 load_row8(const uint16_t* __restrict__ W, int n, int N, int k, int K) {
+// 8 float16 weights of row n at channels k..k+7 (zeros outside the matrix)
+__device__ __forceinline__ uint4 load_raw8(const uint16_t* __restrict__ W, int n, int N, int k, int K) {
+  return (n < N && k < K) ? *reinterpret_cast<const uint4*>(W + (size_t)n * K + k) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ Row8 row8_of(uint4 raw) {
   Row8 o;
-  if (n < N && k < K) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(W + (size_t)n * K + k);
-    const half8_t h = as_half8(raw);
+  const half8_t h = as_half8(raw);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o.v[e] = (float)h[e];
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o.v[e] = 0.0f;
-  }
+  for (int e = 0; e < 8; ++e) o.v[e] = (float)h[e];
   return o;
+}
+
+__device__ __forceinline__ Row8 load_row8(const uint16_t* __restrict__ W, int n, int N, int k, int K) {
+  return row8_of(load_raw8(W, n, N, k, K));
 }
 
 // Act-order columns ("Post-training quantization: GPTQ, AWQ and rotation",
@@ -105,6 +112,9 @@ __device__ __forceinline__ uint32_t pack_dword(const uint32_t nib[8]) {
 }
 
 // GSUB = groups per 128-channel block (4: g = 32, 2: g = 64, 1: g = 128).
+// Without act-order the grid holds only resident wavefronts, and each one walks its
+// units with the next unit's weights already in flight, so loads overlap the coding
+// of the current unit.
 template <int GSUB, bool ASYM, bool PERM = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ W, int N, int K, int S,
                                                           int Gp, int64_t units, uint4* __restrict__ packed,
@@ -116,12 +126,30 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   constexpr int MPG = 4 / GSUB;  // 32-channel steps per group
 
+  uint4 nxt[4];
+  auto fetch = [&](int64_t uu) __attribute__((always_inline)) {
+    if (uu >= units) return;  // uniform
+    const int tt = (int)(uu / S), ss = (int)(uu % S);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) nxt[m] = load_raw8(W, tt * kTileRows + r, N, ss * kSuperK + m * kBlockK + 8 * c, K);
+  };
+  if (!PERM) fetch(wave);
+
   for (int64_t u = wave; u < units; u += nwaves) {
     const int t = (int)(u / S), s = (int)(u % S);
     const int n = t * kTileRows + r;
     Row8 w[4];
+    if (PERM) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) w[m] = load_w8<PERM>(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
+      for (int m = 0; m < 4; ++m) w[m] = load_row8_perm(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
+    } else {
+      uint4 cur[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) cur[m] = nxt[m];
+      fetch(u + nwaves);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) w[m] = row8_of(cur[m]);
+    }
 
     uint32_t dw[4];
 #pragma unroll
@@ -498,6 +526,34 @@ inline int grid_for(int64_t work, int block) {
   return (int)g;
 }
 
+// Workgroups of `block` threads of kernel fn that the current device holds at once.
+int resident_grid(const void* fn, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(fn, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int nb = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  cache[key] = nb * cus;
+  return nb * cus;
+}
+
+// quant_block_kernel without act-order: a persistent grid of resident wavefronts
+template <int GSUB, bool ASYM>
+void launch_block(const QuantArgs& a, int S, int64_t units, hipStream_t stream) {
+  const int block = 256;
+  const void* fn = reinterpret_cast<const void*>(&quant_block_kernel<GSUB, ASYM, false>);
+  const int grid = std::min(grid_for(units * kWave, block), resident_grid(fn, block));
+  hipLaunchKernelGGL((quant_block_kernel<GSUB, ASYM, false>), dim3(grid), dim3(block), 0, stream,
+                     static_cast<const uint16_t*>(a.W), a.N, a.K, S, a.Gp, units, static_cast<uint4*>(a.packed),
+                     static_cast<uint16_t*>(a.scales), static_cast<uint8_t*>(a.zeros), nullptr);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
@@ -531,14 +587,14 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
       else
         hipLaunchKernelGGL((quant_block_kernel<1, false, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
     } else if (a.group == 32) {
-      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<4, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
-      else hipLaunchKernelGGL((quant_block_kernel<4, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      if (a.asym) launch_block<4, true>(a, S, units, stream);
+      else launch_block<4, false>(a, S, units, stream);
     } else if (a.group == 64) {
-      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<2, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
-      else hipLaunchKernelGGL((quant_block_kernel<2, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      if (a.asym) launch_block<2, true>(a, S, units, stream);
+      else launch_block<2, false>(a, S, units, stream);
     } else {
-      if (a.asym) hipLaunchKernelGGL((quant_block_kernel<1, true>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
-      else hipLaunchKernelGGL((quant_block_kernel<1, false>), dim3(grid), dim3(block), 0, stream, W, a.N, a.K, S, a.Gp, units, P, Sc, Z, perm);
+      if (a.asym) launch_block<1, true>(a, S, units, stream);
+      else launch_block<1, false>(a, S, units, stream);
     }
   } else {
     const int J = a.group / kSuperK;
