@@ -50,8 +50,12 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 // SIMD serves faster simply takes more units and all of them finish together (the
 // sequencer favours older wavefronts; a static split leaves the youngest ones
 // streaming alone at the end). Each wavefront streams the blocks of codes and
-// scales of its units with P-1 blocks in flight (vector loads retire in order, so
-// only weights ride that pipeline) and reads its activation operands from LDS: the
+// scales of its units through a ring of P stages (vector loads retire in order, so
+// only weights ride that pipeline): INT4 codes with one row tile per wavefront fill
+// the ring in bursts of P/2 consecutive blocks, one half loading while the other
+// is computed (back-to-back loads of neighbouring kilobytes stream faster than
+// the same loads spread out), the other kinds keep a rolling window of P-1 blocks
+// in flight. Activation operands are read from LDS: the
 // workgroup copies its slice of x (all B rows) into LDS once. The x loads are all
 // issued before any weight load, so they are not queued behind the first burst
 // of weights. A finished unit's partial sums (the B real columns only) are parked
@@ -237,9 +241,12 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
       l_j += GSUB;
     }
   };
+  constexpr bool BURST = R == 1 && !Q8;  // ring filled in two halves of H blocks
+  constexpr int H = P / 2;
+  static_assert(!BURST || P % 2 == 0, "the burst ring has two equal halves");
   WStage<R, GSUB, ASYM, NW> buf[P];
 #pragma unroll
-  for (int p = 0; p < P - 1; ++p) load(buf[p]);
+  for (int p = 0; p < (BURST ? H : P - 1); ++p) load(buf[p]);
 
   // 3. x slice -> LDS (elements 2, 3, 6, 7 of every 8 divided by 16 when BIAS: exact
   //    powers of two; channels past K are zero), plus the zero row. With BIAS the
@@ -362,11 +369,26 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
   };
 
   // once a stage has no unit, every later one has none either
-  while (buf[0].unit >= 0) {
+  if constexpr (BURST) {
+    while (buf[0].unit >= 0) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      load(buf[(p + P - 1) % P]);
-      if (buf[p].unit >= 0) compute(buf[p], buf[(p + 1) % P].s);
+      for (int p = H; p < P; ++p) load(buf[p]);
+#pragma unroll
+      for (int p = 0; p < H; ++p)
+        if (buf[p].unit >= 0) compute(buf[p], buf[p + 1].s);
+#pragma unroll
+      for (int p = 0; p < H; ++p) load(buf[p]);
+#pragma unroll
+      for (int p = H; p < P; ++p)
+        if (buf[p].unit >= 0) compute(buf[p], buf[(p + 1) % P].s);
+    }
+  } else {
+    while (buf[0].unit >= 0) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        load(buf[(p + P - 1) % P]);
+        if (buf[p].unit >= 0) compute(buf[p], buf[(p + 1) % P].s);
+      }
     }
   }
 
@@ -714,8 +736,8 @@ int device_cus() {
 
 template <int R, int GSUB, bool ASYM, int XCH, bool Q8 = false>
 hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
-  // pipeline depth (blocks of codes in flight + 1) per row-tile count; INT8
-  // blocks are twice as large
+  // ring stages per row-tile count: INT4 with one row tile, two bursts of 4
+  // blocks; otherwise blocks in flight + 1 (INT8 blocks are twice as large)
   constexpr int P = Q8 ? (R == 1 ? 4 : 3) : (R == 1 ? 8 : 4);
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;

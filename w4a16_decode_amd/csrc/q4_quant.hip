@@ -126,31 +126,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   constexpr int MPG = 4 / GSUB;  // 32-channel steps per group
 
-  uint4 nxt[4];
-  auto fetch = [&](int64_t uu) __attribute__((always_inline)) {
-    if (uu >= units) return;  // uniform
-    const int tt = (int)(uu / S), ss = (int)(uu % S);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) nxt[m] = load_raw8(W, tt * kTileRows + r, N, ss * kSuperK + m * kBlockK + 8 * c, K);
-  };
-  if (!PERM) fetch(wave);
-
-  for (int64_t u = wave; u < units; u += nwaves) {
-    const int t = (int)(u / S), s = (int)(u % S);
-    const int n = t * kTileRows + r;
-    Row8 w[4];
-    if (PERM) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) w[m] = load_row8_perm(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
-    } else {
-      uint4 cur[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) cur[m] = nxt[m];
-      fetch(u + nwaves);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) w[m] = row8_of(cur[m]);
-    }
-
+  // code one unit (tile t, block s) from its 32 weights per lane, store codes and scales
+  auto code_unit = [&](const Row8 (&w)[4], int t, int s) __attribute__((always_inline)) {
     uint32_t dw[4];
 #pragma unroll
     for (int gs = 0; gs < GSUB; ++gs) {
@@ -197,6 +174,67 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
       }
     }
     packed[((size_t)t * S + s) * kWave + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  };
+
+  if constexpr (PERM) {
+    for (int64_t u = wave; u < units; u += nwaves) {
+      const int t = (int)(u / S), s = (int)(u % S);
+      Row8 w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        w[m] = load_row8_perm(W, t * kTileRows + r, N, s * kSuperK + m * kBlockK + 8 * c, K, perm);
+      code_unit(w, t, s);
+    }
+  } else {
+    // units u = wave, wave + nwaves, ...: the (tile, block) cursor advances by a fixed
+    // step, and two register sets alternate so that the next unit's loads are in
+    // flight while the current one is coded
+    const int dt = (int)(nwaves / S), ds = (int)(nwaves % S);
+    auto advance = [&](int& t, int& s) __attribute__((always_inline)) {
+      s += ds;
+      t += dt;
+      if (s >= S) {
+        s -= S;
+        ++t;
+      }
+    };
+    auto fetch = [&](uint4 (&dst)[4], int t, int s) __attribute__((always_inline)) {
+      const int n = t * kTileRows + r;
+      const int k0 = s * kSuperK + 8 * c;
+      const uint16_t* base = W + (size_t)min(n, N - 1) * K + k0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        dst[m] = (n < N && k0 + m * kBlockK < K) ? *reinterpret_cast<const uint4*>(base + m * kBlockK)
+                                                 : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto code_raw = [&](const uint4 (&raw)[4], int t, int s) __attribute__((always_inline)) {
+      Row8 w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) w[m] = row8_of(raw[m]);
+      code_unit(w, t, s);
+    };
+    int64_t u = wave;
+    int t = (int)(u / S), s = (int)(u % S);
+    uint4 ra[4], rb[4];
+    if (u < units) fetch(ra, t, s);
+    while (u < units) {
+      int tn = t, sn = s;
+      advance(tn, sn);
+      const bool more = u + nwaves < units;
+      if (more) fetch(rb, tn, sn);
+      code_raw(ra, t, s);
+      u += nwaves;
+      t = tn;
+      s = sn;
+      if (!more) break;
+      advance(tn, sn);
+      const bool more2 = u + nwaves < units;
+      if (more2) fetch(ra, tn, sn);
+      code_raw(rb, t, s);
+      u += nwaves;
+      t = tn;
+      s = sn;
+    }
   }
 }
 
