@@ -16,6 +16,8 @@
 // the group amax is a butterfly over GL lanes. Rounding as the weight quantizer:
 // float16 scale fp16(fp32(amax) / 7), the quotient rounded half to even (the IEEE
 // float32 quotient's decision, taken without a per-element divide: q4_rtn.h).
+#include <algorithm>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 #include "q4_rtn.h"
@@ -23,21 +25,26 @@
 namespace q4 {
 namespace {
 
+// A persistent grid of resident wavefronts; each walks its 64-chunk pieces with the
+// next piece's 16-byte loads in flight while the current one is coded. Chunk c of the
+// source is its 8 channels at element 8c (token rows are contiguous); its codes go to
+// dword c + (bh * (max_seq - n) + pos) * cpr of the cache, bh = c / (n * cpr).
 template <int GL>
 __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restrict__ src, int n, int d, int64_t max_seq,
                                                        int64_t pos, int64_t chunks, uint32_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int cpr = d / 8;  // chunks of 8 channels per token row
+  const int64_t per_bh = (int64_t)n * cpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // wave-uniform loop: every lane of a wavefront takes part in each butterfly
-  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63); base < chunks; base += stride) {
+  const bool small = chunks <= 0xFFFFFFFFll;
+  auto fetch = [&](int64_t base) __attribute__((always_inline)) {
     const int64_t c = base + lane;
-    const bool valid = c < chunks;
-    const int64_t r = valid ? c / cpr : 0;   // token row of src: (bh, t)
-    const int e8 = valid ? (int)(c - r * cpr) : 0;
-    half8_t h = {};
-    if (valid) h = as_half8(*reinterpret_cast<const uint4*>(src + r * d + 8 * e8));
+    return c < chunks ? *reinterpret_cast<const uint4*>(src + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto code = [&](int64_t base, uint4 raw) __attribute__((always_inline)) {
+    const int64_t c = base + lane;
+    const half8_t h = as_half8(raw);
     float v[8];
     float a = 0.0f;
 #pragma unroll
@@ -55,12 +62,21 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
       const int q = (int)fminf(fmaxf(rtn_quot(v[e], rcp), -8.0f), 7.0f);
       word |= (uint32_t)(q & 0xF) << (4 * e);
     }
-    if (valid) {
-      const int64_t bh = r / n, t = r - bh * n;
-      const int64_t drow = bh * max_seq + pos + t;
-      codes[drow * cpr + e8] = word;
-      if (e8 % GL == 0) scales[drow * (cpr / GL) + e8 / GL] = __builtin_bit_cast(uint16_t, s16);
+    if (c < chunks) {
+      // 32-bit division whenever the indices fit (the usual case)
+      const int64_t bh = small ? (int64_t)((uint32_t)c / (uint32_t)per_bh) : c / per_bh;
+      const int64_t dc = c + (bh * (max_seq - n) + pos) * cpr;  // chunk index in the cache
+      codes[dc] = word;
+      if (c % GL == 0) scales[dc / GL] = __builtin_bit_cast(uint16_t, s16);  // first chunk of a group (GL | cpr)
     }
+  };
+  // wave-uniform loop: every lane of a wavefront takes part in each butterfly
+  int64_t base = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63);
+  uint4 cur = base < chunks ? fetch(base) : make_uint4(0u, 0u, 0u, 0u);
+  for (; base < chunks; base += stride) {
+    const uint4 nxt = base + stride < chunks ? fetch(base + stride) : make_uint4(0u, 0u, 0u, 0u);
+    code(base, cur);
+    cur = nxt;
   }
 }
 
@@ -97,7 +113,14 @@ inline int grid_for(int64_t work, int block) {
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t stream) {
   const int64_t chunks = a.bh * a.n * (a.d / 8);
   const int block = 256;
-  const int grid = grid_for(chunks, block);
+  int nb = 0, cus = 0, dev = 0;
+  const void* fn = a.group == 32 ? reinterpret_cast<const void*>(&kv_quant_kernel<4>)
+                   : a.group == 64 ? reinterpret_cast<const void*>(&kv_quant_kernel<8>)
+                                   : reinterpret_cast<const void*>(&kv_quant_kernel<16>);
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int grid = std::min(grid_for(chunks, block), nb * cus);  // resident workgroups at most
   const uint16_t* src = static_cast<const uint16_t*>(a.src);
   uint32_t* codes = static_cast<uint32_t*>(a.codes);
   uint16_t* sc = static_cast<uint16_t*>(a.scales);
