@@ -102,7 +102,9 @@ size_t q4_groups_count(int64_t out, int64_t in, int32_t group);
  *   s16[n][j] = float16_rne(float32(max_{k in group j} |W[n][k]|) / 7.0f)
  *   q[n][k]   = clamp(rint_half_even(float32(W[n][k]) / float32(s16)), -8, 7),
  *               q = 0 wherever s16 == 0 (an all-zero or underflowing group).
- * IEEE float32 division. Writes q4_packed_bytes(out, in) bytes to `packed`
+ * The codes are those of the IEEE float32 quotient rounded half to even (the
+ * kernel reaches the same decision without a per-weight divide: one reciprocal
+ * per group and an exact tie check). Writes q4_packed_bytes(out, in) bytes to `packed`
  * (16-byte aligned) and q4_groups_count(out, in, group) float16 to `scales`
  * (8-byte aligned), both in device layout, padding included. W: [out][in]
  * float16, 16-byte aligned. */
