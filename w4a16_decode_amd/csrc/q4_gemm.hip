@@ -56,9 +56,13 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 // is computed (back-to-back loads of neighbouring kilobytes stream faster than
 // the same loads spread out), the other kinds keep a rolling window of P-1 blocks
 // in flight. Activation operands are read from LDS: the
-// workgroup copies its slice of x (all B rows) into LDS once. The x loads are all
-// issued before any weight load, so they are not queued behind the first burst
-// of weights. A finished unit's partial sums (the B real columns only) are parked
+// workgroup copies its slice of x (all B rows) into LDS once. The units a
+// wavefront starts with are fixed (wave, wave + W, ...: as many as its first loads
+// can reach, normally one) and only later ones come from the counter, so every
+// wavefront starts streaming as soon as it runs instead of waiting at a barrier for
+// the workgroup's last wavefront to start; the counter is initialised before the
+// barrier that publishes x and used only after it. A finished unit's partial sums
+// (the B real columns only) are parked
 // in LDS under the unit's index; after one barrier at the end they are added over
 // the chunks in chunk order, so the result does not depend on which wavefront ran
 // which unit. With KS > 1 the workgroups write float32 partials to the workspace
@@ -164,23 +168,33 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
     const int k = min(wsb0 * kSuperK + (idx - b * row_chunks) * 8, K - 8);
     xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
   }
-  if (threadIdx.x == 0) *counter = 0;
-  lds_barrier();  // every x load is issued before any weight load; the counter is set
-
-  // 2. the first P-1 blocks of codes / scales. Block addresses are wave-uniform
-  //    (tile base + 1 KiB per block); only the lane offsets live in VGPRs. Loads are
-  //    unconditional: once the units run out the last block is loaded again, which
-  //    keeps the loop free of branches around loads.
+  // 2. the first L blocks of codes / scales (P/2 in the burst ring, else P-1).
+  //    Those loads end at most L / (shortest unit) units, so the first KST grabs of
+  //    each wavefront, which cover them, take units wave + j * W (j < KST) without
+  //    the counter; the counter serves the rest (units from KST * W on) and is used
+  //    only after the barrier that follows the x staging. Block addresses are
+  //    wave-uniform (tile base + 1 KiB per block); only the lane offsets live in
+  //    VGPRs. Loads are unconditional: once the units run out the last block is
+  //    loaded again, which keeps the loop free of branches around loads.
+  constexpr bool BURST = R == 1 && !Q8;  // ring filled in two halves of H blocks
+  constexpr int H = P / 2;
+  static_assert(!BURST || P % 2 == 0, "the burst ring has two equal halves");
+  constexpr int L = BURST ? H : P - 1;
+  const int KST = 1 + L / (nsb / CH);  // nsb >= CH: every chunk is at least one block
+  if (threadIdx.x == 0) *counter = KST * W * 64;
   const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
   const uint32_t w_lane = (uint32_t)lane * 16u;
   const uint32_t s_lane = (uint32_t)crow * 2u;
   int l_unit = 0, l_s = 0, l_send = 0, l_j = 0, l_jr = 0;
   const unsigned char* l_wt[R];
   const unsigned char* l_st[R];
+  int grabs = 0;  // grabs made by this wavefront (uniform)
   auto grab = [&]() __attribute__((always_inline)) {
-    // every lane adds 1 (called with all lanes active), so a grab moves the counter
-    // by 64 and each lane sees a value in [64u, 64u + 63]
-    const int u = __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;
+    // the first KST grabs take units wave + j * W; later ones the counter, where
+    // every lane adds 1 (called with all lanes active), so a grab moves it by 64 and
+    // each lane sees a value in [64u, 64u + 63]
+    const int u = grabs < KST ? wave + grabs * W : __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;
+    ++grabs;
     if (u >= n_units) {
       l_unit = -1;  // the address registers keep the last unit (loads clamp the block)
       return;
@@ -241,12 +255,9 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
       l_j += GSUB;
     }
   };
-  constexpr bool BURST = R == 1 && !Q8;  // ring filled in two halves of H blocks
-  constexpr int H = P / 2;
-  static_assert(!BURST || P % 2 == 0, "the burst ring has two equal halves");
   WStage<R, GSUB, ASYM, NW> buf[P];
 #pragma unroll
-  for (int p = 0; p < (BURST ? H : P - 1); ++p) load(buf[p]);
+  for (int p = 0; p < L; ++p) load(buf[p]);
 
   // 3. x slice -> LDS (elements 2, 3, 6, 7 of every 8 divided by 16 when BIAS: exact
   //    powers of two; channels past K are zero), plus the zero row. With BIAS the
@@ -494,12 +505,15 @@ void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __re
   const int bcol = lane & 15;
   const int kq = lane >> 4;
 
+  // the zero row and the counter are published by the barrier after the first
+  // unit's loads; a wavefront's first unit is fixed (unit `wave`; units are 8
+  // blocks, longer than the P - 1 loads issued before that barrier), later ones come
+  // from the counter
   if (threadIdx.x < kSuperK / 8) *reinterpret_cast<uint4*>(xzero + threadIdx.x * 8) = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x == 0) {
     *bzero = 0.f;
-    *counter = 0;
+    *counter = W * 64;
   }
-  lds_barrier();
 
   // load side: the unit being streamed, its next block and scale group
   const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
@@ -514,8 +528,11 @@ void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __re
     l_st[r] = reinterpret_cast<const unsigned char*>(scales);
   }
   uint4 xn[BMAX][2];  // x of the unit taken last: channels 8 * (lane + 64 i) of its 1024, per batch row
+  bool first = true;
   auto grab = [&]() __attribute__((always_inline)) {
-    const int u = __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;  // all lanes add: +64 per grab
+    // the first unit is `wave`; then the counter, to which all lanes add: +64 per grab
+    const int u = first ? wave : __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;
+    first = false;
     if (u < n_units) {
       l_unit = u;
       const int i = u / CH, c = u - i * CH;
@@ -607,6 +624,7 @@ void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __re
   SStage<R, GSUB, ASYM> buf[P];
 #pragma unroll
   for (int p = 0; p < P - 1; ++p) load(buf[p]);
+  lds_barrier();  // the zero row and the counter (written above) are set
 
   float4_t acc[R];
 #pragma unroll
