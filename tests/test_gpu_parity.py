@@ -229,23 +229,24 @@ def test_gemm_launch_shapes_agree(q4):
 
 @pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
 @pytest.mark.parametrize("g", [32, 64, 128, 256, 1024])
-def test_gemv_streamed_x(q4, g, asym):
-    """B = 1 with two row tiles per wavefront streams x per unit of 1024 channels;
-    ragged rows (N = 300), several units per row block, wavefronts left without
-    work (W = 8 on few units) and the staged-slice kernel (k_splits = 2) agree with
-    the oracle."""
-    B, N, K = 1, 300, 3072
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_gemv_streamed_x(q4, B, g, asym):
+    """B <= 3 with two row tiles per wavefront streams x per unit of 1024 channels
+    (register and LDS room for 1, 2 or 4 rows; B = 3 leaves one unused); ragged rows
+    (N = 300), several units per row block, wavefronts left without work (W = 8 on
+    few units) and the staged-slice kernel (k_splits = 2) agree with the oracle."""
+    N, K = 300, 3072
     W = synth.weight(N, K, seed=g)
     x = synth.activation(B, K, seed=g + 1)
     qw, q_o, s_o, z_o = _check_quant_exact(q4, W, g, asym, device_layout=False)
     ref = _ref_product(x, q_o, s_o, z_o, g)
     xg = to_gpu(x)
     for Wv, KS in ((1, 1), (2, 1), (8, 1), (8, 2)):
-        say(f"  streamed x g={g} asym={asym} W={Wv} KS={KS}")
+        say(f"  streamed x B={B} g={g} asym={asym} W={Wv} KS={KS}")
         y1 = to_np(q4.gemm_config(xg, qw, 2, Wv, KS))
         y2 = to_np(q4.gemm_config(xg, qw, 2, Wv, KS))
         assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "non-deterministic"
-        assert_close(y1, ref, f"g={g} W={Wv} KS={KS}")
+        assert_close(y1, ref, f"B={B} g={g} W={Wv} KS={KS}")
 
 
 @pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])

@@ -174,7 +174,10 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     const bool w4 = B <= 2 && (S <= 32 || (a->q8 && T < 1024 && S <= 64));
     const int W = w4 ? 4 : B <= 4 ? 8 : gemv_max_waves(R, d.group, a->q8);
     int KS = 1;
-    while (KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
+    // two row tiles per wavefront at B <= 3 stream x per unit (no activation slice
+    // to fit in LDS, so no channel split); otherwise the fewest splits whose slice fits
+    const bool streamed = !a->q8 && q4::gemv_streams_x(B, d.Kp, R, 1);
+    while (!streamed && KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
     a->rows_per_wave = R;
     a->waves_per_group = W;
     a->k_splits = KS;
@@ -324,7 +327,10 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
     if (B <= 16) {
       if (col_tiles != 1) return fail(Q4_ERR_UNSUPPORTED, "col_tiles must be 1 for B <= 16");
       a.lds_limit = lds_per_block();
-      if (!gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, asym, a.lds_limit))
+      // the streaming kernel (two row tiles, B <= 3, no split) stages no activation slice
+      const bool streamed = q4::gemv_streams_x((int)B, d.Kp, rows_per_wave, k_splits);
+      if (!streamed &&
+          !gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, asym, a.lds_limit))
         return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: more splits than 128-channel blocks, "
                     "or the activation slice of B=%lld does not fit LDS or the copy",
                     (int)k_splits, (int)waves_per_group, (long long)B);

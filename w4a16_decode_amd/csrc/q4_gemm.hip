@@ -433,7 +433,8 @@ __global__ void reduce_splits_kernel(const float* __restrict__ ws, int KS, int64
 }
 
 // ---------------------------------------------------------------------------------
-// GEMV for B = 1 with the activation streamed per unit.
+// GEMV for B <= 3 with the activation streamed per unit (at B = 4 the per-unit
+// activation loads, half the bytes of the unit's codes, cost more than staging).
 //
 // Same units, counter, partial sums and final reduction as gemv_kernel, but no
 // workgroup-wide copy of x: a unit is always 8 blocks (1024 channels), and the
@@ -472,15 +473,17 @@ struct SStage {
   int meta;
 };
 
-// Register budget: 128 VGPRs (two 8-wavefront workgroups per CU) with one group
-// per block; smaller groups keep more scales in flight and run with 256.
-template <int R, int GSUB, bool ASYM, int P>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSUB == 1 ? 4 : 1, 8)))
+// Register budget: 128 VGPRs (two 8-wavefront workgroups per CU) for one batch row
+// and one group per block; smaller groups (more scales in flight) and 2-3 batch
+// rows (BMAX = 2 or 4: the x registers of a unit grow with them) run with 256 -- the shapes
+// that take this kernel have at most one row block per CU anyway.
+template <int R, int GSUB, bool ASYM, int P, int BMAX = 1>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(BMAX == 1 && GSUB == 1 ? 4 : 1, 8)))
 void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
                         const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K,
                         int T, int S, int Gp, int J, int nRB, uint16_t* __restrict__ y) {
   static_assert(P - 1 <= kUnitBlocks, "a unit must outlast the blocks in flight");
-  constexpr int BMAX = 1;  // one batch row
+  // BMAX: batch rows the unit's x registers and LDS slice are sized for (B <= BMAX)
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MPG = 4 / GSUB;
   constexpr bool BIAS = !ASYM;
@@ -830,9 +833,8 @@ hipError_t launch_gemv_a(const GemmArgs& a, hipStream_t stream) {
   return a.asym ? launch_gemv_g<R, true>(a, stream) : launch_gemv_g<R, false>(a, stream);
 }
 
-template <int R, int GSUB, bool ASYM>
+template <int R, int GSUB, bool ASYM, int BMAX>
 hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
-  constexpr int BMAX = 1;
   constexpr int P = R == 1 ? 8 : 4;
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
@@ -840,7 +842,7 @@ hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
   const int W = std::min(a.waves_per_group, 8);
   const int nRB = (T + R - 1) / R;
   const int CH = S / kUnitBlocks;
-  const void* fn = reinterpret_cast<const void*>(&gemv_stream_kernel<R, GSUB, ASYM, P>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_stream_kernel<R, GSUB, ASYM, P, BMAX>);
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, 0).total;
   const size_t lim = std::max(a.lds_limit, base + unit_bytes * CH);
@@ -852,18 +854,25 @@ hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
   if (n_rb > max_rb) grid = (nRB + max_rb - 1) / max_rb;
   n_rb = (int)((nRB + grid - 1) / grid);
   const size_t lds = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, n_rb * CH).total;
-  hipLaunchKernelGGL((gemv_stream_kernel<R, GSUB, ASYM, P>), dim3((unsigned)grid), dim3(W * kWave), lds,
+  hipLaunchKernelGGL((gemv_stream_kernel<R, GSUB, ASYM, P, BMAX>), dim3((unsigned)grid), dim3(W * kWave), lds,
                      stream, static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
                      a.Gp, J, nRB, static_cast<uint16_t*>(a.y));
   return hipGetLastError();
 }
 
+template <int R, bool ASYM, int BMAX>
+hipError_t launch_gemv_stream_b(const GemmArgs& a, hipStream_t stream) {
+  if (a.group == 32) return launch_gemv_stream_t<R, 4, ASYM, BMAX>(a, stream);
+  if (a.group == 64) return launch_gemv_stream_t<R, 2, ASYM, BMAX>(a, stream);
+  return launch_gemv_stream_t<R, 1, ASYM, BMAX>(a, stream);
+}
+
 template <int R, bool ASYM>
 hipError_t launch_gemv_stream_g(const GemmArgs& a, hipStream_t stream) {
-  if (a.group == 32) return launch_gemv_stream_t<R, 4, ASYM>(a, stream);
-  if (a.group == 64) return launch_gemv_stream_t<R, 2, ASYM>(a, stream);
-  return launch_gemv_stream_t<R, 1, ASYM>(a, stream);
+  if (a.B == 1) return launch_gemv_stream_b<R, ASYM, 1>(a, stream);
+  if (a.B == 2) return launch_gemv_stream_b<R, ASYM, 2>(a, stream);
+  return launch_gemv_stream_b<R, ASYM, 4>(a, stream);
 }
 
 template <int R>
@@ -875,7 +884,7 @@ hipError_t launch_gemv_stream_a(const GemmArgs& a, hipStream_t stream) {
 
 bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
   const int S = Kp / kSuperK;
-  return B == 1 && k_splits == 1 && rows_per_wave == 2 && S % kUnitBlocks == 0;
+  return B >= 1 && B <= 3 && k_splits == 1 && rows_per_wave == 2 && S % kUnitBlocks == 0;
 }
 
 namespace {
