@@ -48,7 +48,8 @@ def _replays_match(run, x, fill_seeds):
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay with seed {seed} differs"
 
 
-@pytest.mark.parametrize("B,N,K", [(1, 8192, 8192), (4, 300, 2048), (40, 256, 4096), (1, 512, 28672)])
+@pytest.mark.parametrize("B,N,K", [(1, 8192, 8192), (2, 8192, 8192), (3, 8192, 28672), (4, 300, 2048), (40, 256, 4096),
+                                   (1, 512, 28672)])
 def test_graph_q4_gemm(q4, B, N, K):
     import torch
 
