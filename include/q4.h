@@ -27,8 +27,9 @@
  *    y = x W^T); x is [B][in] float16; y is [B][out] float16.
  *  - All pointers except `stream` are DEVICE pointers owned by the caller
  *    (q4_actorder_perm, a host helper, is the one exception). The library never
- *    allocates, frees or caches device memory and keeps no global state: calls
- *    are thread-safe and re-entrant.
+ *    allocates, frees or caches device memory; its only global state is a set of
+ *    lock-guarded host caches of device properties (CU counts, occupancy), so
+ *    calls are thread-safe and re-entrant.
  *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
  *    work on it and never synchronize.
  *  - Arguments are validated on the host before any HIP call; a failed check
