@@ -386,33 +386,10 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
 // Symmetric INT8 with one scale per output channel: s = row amax / 127,
 // q = clamp(round(w / s), -127, 127) ("量化：PTQ、GPTQ、AWQ 与 SmoothQuant",
 // charles2530.github.io, the closing quick code example; "模型量化技术工程实践",
-// www.iopencloud.com, section 2.1). Two passes: the row amax needs the whole row
-// before any code. w8_scale_kernel: one wavefront per row (rows past N get scale
-// 0); w8_pack_kernel: one wavefront per 16-row x 128-channel block, which it
-// writes as two 1 KiB halves (lane l = r + 16c stores row r, channels
+// www.iopencloud.com, section 2.1). A code needs its row's amax, so every 16-row
+// tile is read twice: once for the row maxima, then per 16-row x 128-channel block,
+// which is written as two 1 KiB halves (lane l = r + 16c stores row r, channels
 // 64h + 32j + 8c + e at byte 8j + e of its 16 bytes in half h), codes offset by 128.
-
-__global__ __launch_bounds__(256) void w8_scale_kernel(const uint16_t* __restrict__ W, int N, int K, int Np,
-                                                       uint16_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t n = wave; n < Np; n += nwaves) {
-    float a = 0.0f;
-    if (n < N) {
-      const uint16_t* row = W + (size_t)n * K;  // K % 8 == 0: 16-byte aligned rows
-#pragma unroll 4
-      for (int k = lane * 8; k < K; k += kWave * 8) {
-        const half8_t h = as_half8(*reinterpret_cast<const uint4*>(row + k));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf((float)h[e]));
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
-    if (lane == 0) scales[n] = half_bits((_Float16)(a / 127.0f));
-  }
-}
 
 __device__ __forceinline__ uint32_t w8_code(float w, float r) {
   // offset-binary byte q + 128, q = clamp(rint(w / s), -127, 127), r = rtn_recip(s)
@@ -421,29 +398,58 @@ __device__ __forceinline__ uint32_t w8_code(float w, float r) {
   return (uint32_t)((int)q + 128);
 }
 
-__global__ __launch_bounds__(256) void w8_pack_kernel(const uint16_t* __restrict__ W, int N, int K, int S,
-                                                      int64_t units, const uint16_t* __restrict__ scales,
-                                                      uint4* __restrict__ packed) {
+// Both reads in one kernel: a workgroup of 8 wavefronts takes one 16-row tile at a
+// time (persistent; two workgroups per CU). Wavefront w reduces the maxima of rows
+// 2w and 2w+1 (8 loads of 16 bytes per lane in flight; rows past N get scale 0),
+// the 16 reciprocal scales go through LDS, then wavefront w codes blocks w, w + 8,
+// ... of the tile, re-reading it while it is still in the caches (two tiles per CU
+// are in flight), so W mostly crosses HBM once.
+__global__ __launch_bounds__(512) void w8_fused_kernel(const uint16_t* __restrict__ W, int N, int K, int S, int T,
+                                                       uint16_t* __restrict__ scales, uint4* __restrict__ packed) {
+  __shared__ float rcp_s[kTileRows];
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;  // 0 .. 7
   const int r = lane & 15, c = lane >> 4;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t u = wave; u < units; u += nwaves) {
-    const int t = (int)(u / S), s = (int)(u % S);
-    const int n = t * kTileRows + r;
-    const float rcp = rtn_recip((float)__builtin_bit_cast(_Float16, scales[n]));
-    uint32_t d[8];
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int n = t * kTileRows + 2 * wave + rr;
+      float a = 0.0f;
+      if (n < N) {
+        const uint16_t* row = W + (size_t)n * K;  // K % 8 == 0: 16-byte aligned rows
+#pragma unroll 8
+        for (int k = lane * 8; k < K; k += kWave * 8) {
+          const half8_t h = as_half8(*reinterpret_cast<const uint4*>(row + k));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        d[2 * m + i] = w8_code(w.v[4 * i], rcp) | (w8_code(w.v[4 * i + 1], rcp) << 8) |
-                       (w8_code(w.v[4 * i + 2], rcp) << 16) | (w8_code(w.v[4 * i + 3], rcp) << 24);
+          for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf((float)h[e]));
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
+      const _Float16 s16 = (_Float16)(a / 127.0f);  // rows past N: 0
+      if (lane == 0) {
+        scales[n] = half_bits(s16);
+        rcp_s[2 * wave + rr] = rtn_recip((float)s16);
+      }
     }
-    uint4* out = packed + ((size_t)t * S + s) * 2 * kWave + lane;
-    out[0] = make_uint4(d[0], d[1], d[2], d[3]);
-    out[kWave] = make_uint4(d[4], d[5], d[6], d[7]);
+    __syncthreads();
+    const float rcp = rcp_s[r];
+    const int n = t * kTileRows + r;
+    for (int s = wave; s < S; s += 8) {
+      uint32_t d[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const Row8 w = load_row8(W, n, N, s * kSuperK + m * kBlockK + 8 * c, K);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          d[2 * m + i] = w8_code(w.v[4 * i], rcp) | (w8_code(w.v[4 * i + 1], rcp) << 8) |
+                         (w8_code(w.v[4 * i + 2], rcp) << 16) | (w8_code(w.v[4 * i + 3], rcp) << 24);
+      }
+      uint4* out = packed + ((size_t)t * S + s) * 2 * kWave + lane;
+      out[0] = make_uint4(d[0], d[1], d[2], d[3]);
+      out[kWave] = make_uint4(d[4], d[5], d[6], d[7]);
+    }
+    __syncthreads();  // rcp_s is rewritten for the next tile
   }
 }
 
@@ -685,12 +691,13 @@ hipError_t launch_quantize_w8(const W8Args& a, hipStream_t stream) {
   const int S = a.Kp / kSuperK;
   const int T = a.Np / kTileRows;
   const int block = 256;
-  hipLaunchKernelGGL(w8_scale_kernel, dim3(grid_for((int64_t)a.Np * kWave, block)), dim3(block), 0, stream,
-                     static_cast<const uint16_t*>(a.W), a.N, a.K, a.Np, static_cast<uint16_t*>(a.scales));
-  const int64_t units = (int64_t)T * S;
-  hipLaunchKernelGGL(w8_pack_kernel, dim3(grid_for(units * kWave, block)), dim3(block), 0, stream,
-                     static_cast<const uint16_t*>(a.W), a.N, a.K, S, units, static_cast<const uint16_t*>(a.scales),
-                     static_cast<uint4*>(a.packed));
+  (void)block;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int grid = std::max(1, std::min(T, 2 * cus));
+  hipLaunchKernelGGL(w8_fused_kernel, dim3(grid), dim3(512), 0, stream, static_cast<const uint16_t*>(a.W), a.N, a.K,
+                     S, T, static_cast<uint16_t*>(a.scales), static_cast<uint4*>(a.packed));
   return hipGetLastError();
 }
 
