@@ -344,6 +344,30 @@ def test_full_batch_sweep_28672x8192(q4):
     _full_size_check(q4, 28672, 8192, 128, (1, 4, 16, 32, 64, 128, 256), seed=4, nrows=64)
 
 
+def test_full_fused_gate_up_batches(q4):
+    """The fused 70B gate/up matrix (57344x8192, device-generated weights) at B = 16,
+    64, 128 and 256: B = 128 takes the wider column groups that keep its skinny-GEMM
+    grid within one round of workgroups; codes, scales and products on sampled rows."""
+    import torch
+
+    N, K, g = 57344, 8192, 128
+    say(f"fused gate/up {N}x{K} batches")
+    Wd = synth.device_weight(N, K, seed=6, layer=0, matrix=0)
+    qw = q4.quantize_pack(Wd, g)
+    rows = _sampled_rows(N, 64, 7)
+    W = to_np(Wd[torch.from_numpy(rows).cuda()])
+    del Wd
+    q_o, s_o = oracle.quantize_sym(W, g)
+    c, sc, _ = q4.to_canonical(qw)
+    assert np.array_equal(to_np(c[torch.from_numpy(rows).cuda()]), oracle.pack_canonical(q_o))
+    assert np.array_equal(to_np(sc[torch.from_numpy(rows).cuda()]).view(np.uint16), s_o.view(np.uint16))
+    for B in (16, 64, 128, 256):
+        x = synth.activation(B, K, seed=B)
+        y = to_np(q4.gemm(to_gpu(x), qw))
+        rel, mx = assert_close(y[:, rows], _ref_product(x, q_o, s_o, None, g), f"gate/up B={B}")
+        say(f"  B={B}: rel L2 {rel:.2e} max {mx:.2e}")
+
+
 @pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
 @pytest.mark.parametrize("g", [32, 64, 128])
 def test_full_heavy_tailed_gemv(q4, g, asym):

@@ -190,6 +190,33 @@ def test_w8_full_batch_28672x8192(q4):
     _full_w8(q4, 28672, 8192, (1, 16, 32, 64, 256), seed=4, nrows=64)
 
 
+def test_w8_full_fused_gate_up_b128(q4):
+    """The fused 70B gate/up matrix (57344x8192, device-generated weights) at B = 128,
+    where the skinny GEMM takes wider column groups to stay within one round of
+    workgroups, and at B = 64 and 256 beside it; codes, scales, products on sampled rows."""
+    import torch
+
+    N, K = 57344, 8192
+    say(f"w8 fused gate/up {N}x{K}")
+    Wd = synth.device_weight(N, K, seed=6, layer=0, matrix=1)
+    qw = q4.q8_quantize_pack(Wd)
+    r = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, N - 1], r.choice(N, size=64, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    W = to_np(Wd[idx])
+    del Wd
+    q_o, s_o = oracle.quantize_w8(W)
+    c, s = q4.q8_to_canonical(qw)
+    assert np.array_equal(to_np(c[idx]), q_o)
+    assert np.array_equal(to_np(s[idx]).view(np.uint16), s_o.view(np.uint16))
+    for B in (64, 128, 256):
+        x = synth.activation(B, K, seed=B + 1)
+        y = to_np(q4.q8_gemm(to_gpu(x), qw))
+        rel, mx = assert_close(y[:, rows], oracle.gemm_w8_rows(x, q_o, s_o, np.arange(len(rows))),
+                               f"w8 gate/up B={B}")
+        say(f"  w8 gate/up B={B}: rel L2 {rel:.2e} max {mx:.2e}")
+
+
 def test_w8_full_heavy_tailed(q4):
     say("w8 heavy-tailed 14336x4096")
     _full_w8(q4, 14336, 4096, (1, 4), seed=5, heavy=True)

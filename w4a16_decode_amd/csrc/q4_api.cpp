@@ -186,7 +186,8 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
   }
   // B > 16: skinny MFMA GEMM, 8 wavefronts per workgroup sharing CT column tiles of
   // 16 batch rows (double-buffered activation chunks in LDS): 2 column tiles up to
-  // B = 32, 4 up to 128, else 8; 2 row tiles per wavefront; the channel range split
+  // B = 32, 4 up to 128 (8 when that needs more than 256 workgroups), else 8; 2 row
+  // tiles per wavefront; the channel range split
   // over up to 4 workgroups until there are about 256 of them, with 1 row tile per
   // wavefront when even that leaves too few. (Measured on the Llama-3-70B shapes.)
   int CT = col_tiles_total <= 2 ? 2 : (col_tiles_total <= 8 ? 4 : 8);
@@ -198,6 +199,11 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     else if (CT > 2) CT /= 2;
     else break;  // unreachable: R = 1, CT = 2 always fits
   }
+  // one workgroup per CU (its activation buffers take ~132 KiB of LDS): where the
+  // grid would need a second, partial round (57344 rows at B = 128: 448 workgroups),
+  // wider column groups halve it (gate/up at B = 128: INT4 175 -> 149 us, INT8
+  // 215 -> 168 us)
+  while (CT < 8 && CT < col_tiles_total && wgs(R) > 256 && mfma_shape_ok(R, 8, 1, CT * 2, d.group, S, a->q8)) CT *= 2;
   int KS = (int)std::min<int64_t>(4, std::max<int64_t>(1, 256 / wgs(R)));
   while (KS > 1 && !mfma_shape_ok(R, 8, KS, CT, d.group, S, a->q8)) --KS;
   a->col_tiles = CT;
