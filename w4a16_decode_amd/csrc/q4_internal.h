@@ -88,8 +88,12 @@ hipError_t launch_w8_from_canonical(const W8Args& a, hipStream_t stream);
 hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
-// Whether the GEMV for this shape streams x per unit (B = 1, one split, two row tiles
-// per wavefront, a multiple of 1024 channels) instead of staging the whole slice.
+// Whether the GEMV for this shape streams x per unit (B <= 3, one split, two row
+// tiles per wavefront, a multiple of 1024 channels) instead of staging the whole slice.
 bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits);
+// Compute units of the current device, and the workgroups of `block` threads of
+// kernel fn it holds at once (both cached, lock-guarded).
+int device_cu_count_cached();
+int resident_grid(const void* fn, int block);
 
 }  // namespace q4

@@ -113,14 +113,10 @@ inline int grid_for(int64_t work, int block) {
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t stream) {
   const int64_t chunks = a.bh * a.n * (a.d / 8);
   const int block = 256;
-  int nb = 0, cus = 0, dev = 0;
   const void* fn = a.group == 32 ? reinterpret_cast<const void*>(&kv_quant_kernel<4>)
                    : a.group == 64 ? reinterpret_cast<const void*>(&kv_quant_kernel<8>)
                                    : reinterpret_cast<const void*>(&kv_quant_kernel<16>);
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  const int grid = std::min(grid_for(chunks, block), nb * cus);  // resident workgroups at most
+  const int grid = std::min(grid_for(chunks, block), resident_grid(fn, block));  // resident workgroups at most
   const uint16_t* src = static_cast<const uint16_t*>(a.src);
   uint32_t* codes = static_cast<uint32_t*>(a.codes);
   uint16_t* sc = static_cast<uint16_t*>(a.scales);

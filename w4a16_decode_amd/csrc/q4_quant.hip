@@ -23,6 +23,42 @@
 #include "q4_rtn.h"
 
 namespace q4 {
+
+// Compute units of the current device (cached per device).
+int device_cu_count_cached() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+// Workgroups of `block` threads of kernel fn that the current device holds at once
+// (cached per kernel and device).
+int resident_grid(const void* fn, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(std::make_pair(fn, dev));
+    if (it != cache.end()) return it->second;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
+  const int grid = nb * device_cu_count_cached();
+  std::lock_guard<std::mutex> lk(mu);
+  cache[std::make_pair(fn, dev)] = grid;
+  return grid;
+}
+
 namespace {
 
 struct Row8 {
@@ -570,23 +606,6 @@ inline int grid_for(int64_t work, int block) {
   return (int)g;
 }
 
-// Workgroups of `block` threads of kernel fn that the current device holds at once.
-int resident_grid(const void* fn, int block) {
-  static std::mutex mu;
-  static std::map<std::pair<const void*, int>, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  std::lock_guard<std::mutex> lk(mu);
-  const auto key = std::make_pair(fn, dev);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int nb = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  cache[key] = nb * cus;
-  return nb * cus;
-}
-
 // quant_block_kernel without act-order: a persistent grid of resident wavefronts
 template <int GSUB, bool ASYM>
 void launch_block(const QuantArgs& a, int S, int64_t units, hipStream_t stream) {
@@ -692,10 +711,7 @@ hipError_t launch_quantize_w8(const W8Args& a, hipStream_t stream) {
   const int T = a.Np / kTileRows;
   const int block = 256;
   (void)block;
-  int cus = 0, dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  const int grid = std::max(1, std::min(T, 2 * cus));
+  const int grid = std::max(1, std::min(T, 2 * device_cu_count_cached()));
   hipLaunchKernelGGL(w8_fused_kernel, dim3(grid), dim3(512), 0, stream, static_cast<const uint16_t*>(a.W), a.N, a.K,
                      S, T, static_cast<uint16_t*>(a.scales), static_cast<uint4*>(a.packed));
   return hipGetLastError();
