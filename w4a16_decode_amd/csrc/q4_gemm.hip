@@ -16,10 +16,11 @@
 //    pair, see dequant8), so the MFMA contracts the integer codes against float16 x
 //    with float32 accumulation; each group's partial is scaled in float32.
 //  * The batch (B <= 16) fills the 16 MFMA columns of the GEMV; its wavefronts
-//    split the channel range and their partial sums are reduced through LDS in a
-//    fixed order (deterministic). Larger B runs the skinny GEMM: 2 to 8 column
-//    tiles of 16 batch rows per workgroup, staged through LDS and shared by its
-//    four wavefronts, each owning whole row tiles.
+//    take units of (row tiles x a chunk of the channel range, usually 1024
+//    channels) and their partial sums are
+//    reduced through LDS in a fixed order (deterministic). Larger B runs the skinny
+//    GEMM: 2 to 8 column tiles of 16 batch rows per workgroup, staged through LDS
+//    and shared by its 8 (or 4) wavefronts, each owning whole row tiles.
 #include <algorithm>
 #include <map>
 #include <mutex>
