@@ -146,6 +146,8 @@ def _prep_gemm(x, qw: QuantizedWeight, out):
     _require_gpu(x, "x", torch.float16)
     if x.dim() != 2 or x.shape[1] != qw.in_features:
         raise ValueError(f"x must be [B, {qw.in_features}]")
+    if qw.packed.device != x.device or qw.scales.device != x.device:
+        raise ValueError(f"x ({x.device}) and the weights ({qw.packed.device}) must be on the same GPU")
     B = x.shape[0]
     if out is None:
         out = torch.empty((B, qw.out_features), dtype=torch.float16, device=x.device)
@@ -153,6 +155,8 @@ def _prep_gemm(x, qw: QuantizedWeight, out):
         _require_gpu(out, "out", torch.float16)
         if tuple(out.shape) != (B, qw.out_features):
             raise ValueError(f"out must be [{B}, {qw.out_features}]")
+        if out.device != x.device:
+            raise ValueError(f"out ({out.device}) must be on x's GPU ({x.device})")
     return B, out
 
 
@@ -314,6 +318,8 @@ def gemm_perm(x, aw: ActOrderWeight, out=None, workspace=None):
     """q4_gemm_perm: y = x . W_hat^T for act-order weights (x gathered through perm)."""
     qw = aw.qw
     B, out = _prep_gemm(x, qw, out)
+    if aw.perm.device != x.device:
+        raise ValueError(f"perm ({aw.perm.device}) must be on x's GPU ({x.device})")
     lib = _lib.load()
     need = int(lib.q4_workspace_bytes_perm(B, qw.out_features, qw.in_features, qw.group)) if B > 0 else 0
     ws_ptr, ws_bytes = _workspace(x, need, workspace)
@@ -366,6 +372,8 @@ def kv_quantize_pack(src, cache: KVCache4, pos: int) -> None:
         raise ValueError("src must be [batch, heads, n, head_dim] or [bh, n, head_dim]")
     if bh != cache.codes.shape[0] or d != cache.head_dim:
         raise ValueError("src does not match the cache's sequences or head_dim")
+    if src.device != cache.codes.device:
+        raise ValueError(f"src ({src.device}) and the cache ({cache.codes.device}) must be on the same GPU")
     _check(_lib.load().q4_kv_quantize_pack(src.data_ptr(), bh, n, d, cache.group, cache.codes.data_ptr(),
                                            cache.scales.data_ptr(), cache.max_seq, pos, _stream(src)))
 
