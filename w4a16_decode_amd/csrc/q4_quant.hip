@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <tuple>
 
 #include "q4_device.h"
 #include "q4_internal.h"
@@ -43,19 +44,20 @@ int device_cu_count_cached() {
 // (cached per kernel and device).
 int resident_grid(const void* fn, int block) {
   static std::mutex mu;
-  static std::map<std::pair<const void*, int>, int> cache;
+  static std::map<std::tuple<const void*, int, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const auto key = std::make_tuple(fn, block, dev);
   {
     std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(std::make_pair(fn, dev));
+    auto it = cache.find(key);
     if (it != cache.end()) return it->second;
   }
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
   const int grid = nb * device_cu_count_cached();
   std::lock_guard<std::mutex> lk(mu);
-  cache[std::make_pair(fn, dev)] = grid;
+  cache[key] = grid;
   return grid;
 }
 
