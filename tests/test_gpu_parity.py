@@ -278,6 +278,28 @@ def test_gemm_mfma_shapes_agree(q4, B, g, asym):
     assert ran >= 3
 
 
+@pytest.mark.parametrize("B,N,K", [(4, 1000, 28672), (32, 4096, 8192), (6, 998, 28672)])
+def test_split_sum_any_output_alignment(q4, B, N, K):
+    """Products whose channel range is split over workgroups (float32 partials added
+    by a second kernel: 8 outputs per thread when y is 16-byte aligned and B * N a
+    multiple of 8, one per thread otherwise) give the same bits into an aligned output
+    and into one that is only 2-byte aligned, and match the oracle."""
+    import torch
+
+    W = synth.weight(N, K, seed=40)
+    x = synth.activation(B, K, seed=41)
+    qw = q4.quantize_pack(to_gpu(W), 128)
+    assert q4.workspace_bytes(B, N, K, 128) > 0, "shape must take a channel split"
+    y_al = q4.gemm(to_gpu(x), qw)
+    buf = torch.empty(B * N + 8, dtype=torch.float16, device="cuda")
+    y_un = buf[1:1 + B * N].view(B, N)
+    assert y_un.data_ptr() % 16 == 2
+    q4.gemm(to_gpu(x), qw, out=y_un)
+    assert torch.equal(y_al.view(torch.int16), y_un.view(torch.int16))
+    q_o, s_o = oracle.quantize_sym(W, 128)
+    assert_close(to_np(y_al), _ref_product(x, q_o, s_o, None, 128), f"split sum B={B} N={N} K={K}")
+
+
 def test_gemm_empty_batch(q4):
     import torch
 
