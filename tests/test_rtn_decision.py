@@ -1,12 +1,14 @@
 """The quantize kernels' division-free code decision, modelled in numpy float32.
 
-The kernels round w / s half to even (float16 w and s) from r = fl(1 / s) and
-t = fl(w * r): where t lies within 2^-14 of h = floor(t) + 1/2 the code is rint(h),
-else rint(t). These tests check that this decision equals the rounding of the IEEE
-float32 quotient that the pages' formula q = round(w / scale) is taken as ("LLM
-后训练量化深度实战…", www.ybb.press, section 二), for every finite float16 w against a
-spread of float16 scales, every exact tie, and the range limit |w / s| < 512, in
-both evaluation orders of t - h (rounded product, or fused multiply-add).
+The kernels round w / s half to even (float16 w and s) from a reciprocal r of s
+(the hardware reciprocal, within one ulp of 1 / s) and t = fl(w * r): where t lies
+within 2^-14 of h = floor(t) + 1/2 the code is rint(h), else rint(t). These tests
+check that this decision equals the rounding of the IEEE float32 quotient that the
+pages' formula q = round(w / scale) is taken as ("LLM 后训练量化深度实战…",
+www.ybb.press, section 二), for every finite float16 w against a spread of float16
+scales, every exact tie, and the range limit |w / s| < 341, in both evaluation
+orders of t - h (rounded product, or fused multiply-add) and with r the correctly
+rounded 1 / s or either float32 neighbour of it.
 """
 
 from fractions import Fraction
@@ -33,9 +35,19 @@ def _scales(n_random=160, seed=5):
     return np.unique(np.concatenate([picks, special]))
 
 
-def _model(w32, s32, fused):
-    """The kernels' arithmetic in float32 (fused: t - h from the exact product w * r)."""
+ULPS = [0, -1, 1]  # r = fl(1 / s) moved by this many float32 steps (one-ulp reciprocal)
+
+
+def _recip(s32, ulp):
     r = np.float32(1.0) / s32
+    for _ in range(abs(ulp)):
+        r = np.nextafter(r, np.float32(np.inf) if ulp > 0 else np.float32(0))
+    return np.float32(r)
+
+
+def _model(w32, s32, fused, ulp=0):
+    """The kernels' arithmetic in float32 (fused: t - h from the exact product w * r)."""
+    r = _recip(s32, ulp)
     t = w32 * r
     h = np.floor(t) + np.float32(0.5)
     if fused:
@@ -45,22 +57,24 @@ def _model(w32, s32, fused):
     return np.rint(np.where(np.abs(d) < BAND, h, t))
 
 
+@pytest.mark.parametrize("ulp", ULPS)
 @pytest.mark.parametrize("fused", [False, True])
-def test_decision_equals_ieee_quotient_all_fp16(fused):
+def test_decision_equals_ieee_quotient_all_fp16(fused, ulp):
     w = _all_finite_fp16().astype(np.float32)
     for s16 in _scales():
         s32 = np.float32(s16)
         ref = np.rint(w / s32)
-        got = _model(w, s32, fused)
-        inside = np.abs(ref) < 511
+        got = _model(w, s32, fused, ulp)
+        inside = np.abs(ref) < 340
         bad = inside & (got != ref)
-        assert not bad.any(), (float(s16), w[bad][:4])
+        assert not bad.any(), (float(s16), ulp, w[bad][:4])
         # past the range the decision may differ by one but stays beyond every clamp bound
-        assert np.all(np.abs(got[~inside]) >= 510)
+        assert np.all(np.abs(got[~inside]) >= 339)
 
 
+@pytest.mark.parametrize("ulp", ULPS)
 @pytest.mark.parametrize("fused", [False, True])
-def test_exact_ties_round_to_even(fused):
+def test_exact_ties_round_to_even(fused, ulp):
     checked = 0
     for s16 in _scales():
         s = Fraction(float(s16))
@@ -69,7 +83,7 @@ def test_exact_ties_round_to_even(fused):
             w16 = np.float16(float(w_exact))
             if not np.isfinite(w16) or Fraction(float(w16)) != w_exact:
                 continue  # not a float16 value
-            got = _model(np.array([w16], dtype=np.float32), np.float32(s16), fused)[0]
+            got = _model(np.array([w16], dtype=np.float32), np.float32(s16), fused, ulp)[0]
             even = k if k % 2 == 0 else k + 1
             assert got == even, (float(s16), float(w16))
             checked += 1
