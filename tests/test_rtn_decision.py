@@ -110,3 +110,16 @@ def test_zero_scale_gives_code_zero():
     t = w * np.float32(0.0)
     h = np.floor(t) + np.float32(0.5)
     assert np.all(np.rint(np.where(np.abs(t - h) < BAND, h, t)) == 0)
+
+
+@pytest.mark.parametrize("d", [7, 127])
+def test_scale_from_reciprocal_constant(d):
+    # the INT4 (amax / 7), KV (amax / 7) and INT8 (amax / 127) scales are formed as
+    # fp16(amax * fl(1 / d)) instead of fp16(fl(amax / d)): equal for every positive
+    # float16 amax (the float32 multiply is correctly rounded, so this model is exact)
+    a = _all_finite_fp16()
+    a = a[a > 0].astype(np.float32)
+    c = np.float32(1.0) / np.float32(d)
+    ref = (np.maximum(a, np.float32(1e-12)) / np.float32(d)).astype(np.float16)
+    got = (np.maximum(a, np.float32(1e-12)) * c).astype(np.float16)
+    assert np.array_equal(ref.view(np.uint16), got.view(np.uint16))

@@ -128,7 +128,10 @@ __device__ __forceinline__ float wave_min4(float a) {
 __device__ __forceinline__ uint16_t half_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
 // Symmetric scale of a group from its amax (float32 IEEE divide, RNE to float16).
-__device__ __forceinline__ _Float16 sym_scale(float amax) { return (_Float16)(fmaxf(amax, 1e-12f) / 7.0f); }
+// fp16(fp32(amax) / 7) for a float16-valued amax: the product with the float32 constant
+// fl(1/7) rounds to the same float16 for every positive float16 amax (checked for all
+// of them on the host), so no divide is needed
+__device__ __forceinline__ _Float16 sym_scale(float amax) { return (_Float16)(fmaxf(amax, 1e-12f) * (1.0f / 7.0f)); }
 
 // r = rtn_recip(s): 0 for s == 0, which gives the code of q = 0 (and z = 0)
 __device__ __forceinline__ uint32_t sym_code(float w, float r) {
@@ -464,7 +467,9 @@ __global__ __launch_bounds__(512) void w8_fused_kernel(const uint16_t* __restric
       }
 #pragma unroll
       for (int m = 1; m < kWave; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
-      const _Float16 s16 = (_Float16)(a / 127.0f);  // rows past N: 0
+      // fp16(fp32(amax) / 127) through the constant fl(1/127): the same float16 for every
+      // float16 amax (checked for all of them on the host); rows past N: 0
+      const _Float16 s16 = (_Float16)(a * (1.0f / 127.0f));
       if (lane == 0) {
         scales[n] = half_bits(s16);
         rcp_s[2 * wave + rr] = rtn_recip((float)s16);
