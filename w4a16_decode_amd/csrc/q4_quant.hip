@@ -197,7 +197,9 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
         hi = wave_max4(hi);
         s16 = (_Float16)((hi - lo) / 15.0f);
         scale_f = (float)s16;
-        if (scale_f != 0.0f) zero_f = fminf(fmaxf(rintf(-lo / scale_f), 0.0f), 15.0f);
+        // z = clamp(rint(-lo / s), 0, 15) by the same exact decision as the codes (-lo
+        // is a float16 value); s == 0 gives z = 0
+        zero_f = fminf(fmaxf(rtn_quot(-lo, rtn_recip(scale_f)), 0.0f), 15.0f);
       }
       const float rcp = rtn_recip(scale_f);
 #pragma unroll
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const uint16_t* __restr
       hi = wave_max4(hi);
       s16 = (_Float16)((hi - lo) / 15.0f);
       scale_f = (float)s16;
-      if (scale_f != 0.0f) zero_f = fminf(fmaxf(rintf(-lo / scale_f), 0.0f), 15.0f);
+      zero_f = fminf(fmaxf(rtn_quot(-lo, rtn_recip(scale_f)), 0.0f), 15.0f);  // as in quant_block_kernel
     }
     const float rcp = rtn_recip(scale_f);
     for (int sb = 0; sb < J; ++sb) {
