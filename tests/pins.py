@@ -18,6 +18,7 @@ from fractions import Fraction
 
 import numpy as np
 
+import exact_round as xr  # noqa: E402
 import synth  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -261,6 +262,62 @@ def pin_asym_exact_grid(seed=7):
     assert np.array_equal(o.dequant_asym(q, s16, z, g), W.astype(np.float64))
 
 
+def _asym_pairs(n=100_000, seed=61):
+    """float16 (min, max) pairs: straddling zero, one-sided on either side, equal,
+    and hand-picked ones whose float32 range is not a float16 value (so rounding
+    the range to float16 first would move the scale) or exceeds the float16 range."""
+    r = np.random.default_rng(seed)
+    neg = r.integers(0x8000, 0xFBFF, size=n, endpoint=True).astype(np.uint16).view(np.float16)
+    pos = r.integers(0x0000, 0x7BFF, size=n, endpoint=True).astype(np.uint16).view(np.float16)
+    a, b = neg.copy(), pos.copy()
+    k = n // 7
+    a[:k], b[:k] = pos[:k], pos[k:2 * k]                   # both >= 0: z clamps to 0
+    a[k:2 * k], b[k:2 * k] = neg[:k], neg[k:2 * k]         # both <= 0: z clamps to 15
+    mn, mx = np.minimum(a, b), np.maximum(a, b)
+    hand = [(-2.0 ** -14, 1.0), (-0.3, 1000.7), (-65504.0, 65504.0), (-60000.0, 30000.0), (0.0, 0.0),
+            (1.5, 1.5), (-2.0 ** -24, 2.0 ** -24), (-1.0, 2.0 ** -13), (-3.0, 5.0), (-7.5, 7.5)]
+    hm = np.array([h[0] for h in hand], dtype=np.float16)
+    hx = np.array([h[1] for h in hand], dtype=np.float16)
+    return np.concatenate([hm, mn]), np.concatenate([hx, mx])
+
+
+def pin_asym_scale_zero_exact(g=8, seed=62):
+    """Reading R5 step by step in exact integer arithmetic, on 10^5 float16 (min, max)
+    pairs: range = fl32(fl32(max) - fl32(min)), s16 = fp16(fl32(range / 15)),
+    z = clamp(rint(-min / s16), 0, 15), q = clamp(rint(w / s16) + z, 0, 15) with
+    rint half to even of the exact rational quotient, q = z = 0 where s16 == 0
+    ([ARG] section 二.2; [WIKI] section 7.4.1.1). Each group holds its min, its max
+    and g - 2 values drawn between them."""
+    o = _orc()
+    mn, mx = _asym_pairs()
+    G = mn.size
+    r = np.random.default_rng(seed)
+    lo, hi = mn.astype(np.float64)[:, None], mx.astype(np.float64)[:, None]
+    mid = (lo + (hi - lo) * r.random((G, g - 2))).astype(np.float16)
+    W = np.concatenate([mn[:, None], mid, mx[:, None]], axis=1)
+    W = np.take_along_axis(W, r.permuted(np.tile(np.arange(g), (G, 1)), axis=1), axis=1)
+    q, s16, z = o.quantize_asym(W, g)
+    # the range: an exact integer on the 2^-24 grid, rounded once to float32
+    D = xr.on_grid(mx) - xr.on_grid(mn)
+    Qr, Tr = xr.round_to(D, -24, False, xr.FP32)
+    # / 15 rounded to float32, then to float16
+    Qd, Td, st = xr.divide(Qr, Tr, 15)
+    Q32, T32 = xr.round_to(Qd, Td, st, xr.FP32)
+    Q16, T16 = xr.round_to(Q32, T32, False, xr.FP16)
+    s_exp = xr.to_float64(Q16, T16)
+    got = s16[:, 0].astype(np.float64)
+    assert np.array_equal(got, s_exp), np.flatnonzero(got != s_exp)[:5]
+    # z and q from exact integer quotients: w / s16 = (w * 2^24) / (Q16 * 2^(T16 + 24))
+    S = np.where(Q16 > 0, Q16 << np.maximum(T16 + 24, 0), 1)
+    zero = Q16 == 0
+    z_exp = np.where(zero, 0, np.clip(xr.rint_div(-xr.on_grid(mn), S), 0, 15))
+    assert np.array_equal(z[:, 0].astype(np.int64), z_exp)
+    Wi = xr.on_grid(W)
+    q_exp = np.clip(xr.rint_div(Wi, S[:, None]) + z_exp[:, None], 0, 15)
+    q_exp = np.where(zero[:, None], 0, q_exp)
+    assert np.array_equal(q.astype(np.int64), q_exp)
+
+
 def pin_asym_invariants(N=64, K=1024, g=64, seed=9):
     """Asymmetric bounds: codes in [0,15], the group min maps to code 0 when z is
     unclamped, |w - w_hat| <= s16/2 below the clamp and <= 1.5*s16 at it."""
@@ -493,6 +550,35 @@ def pin_clip_exact_bruteforce(seed=22):
                 assert q[n, j * g:(j + 1) * g].tolist() == best[2]
                 assert s[n, j].view(np.uint16) == best[3].view(np.uint16)
         assert p[0, 0] == 100 and s[0, 0] == 0 and p[1, 0] == 100
+
+
+def pin_clip_scale_steps_exact(n_amax=10_000, seed=63):
+    """Reading C2's scale, each rounding step redone in exact integer arithmetic for
+    every percent p in 1..100 and 10^4 float16 amax (all normal and subnormal
+    binades): alpha = fl32(p / 100), a = fl32(fl32(amax) * alpha), a = max(a, fl32(1e-12)),
+    s16 = fp16(fl32(a / 7)) ([ARG] section 三.2 with the RTN scale of [YBB] section 二)."""
+    o = _orc()
+    r = np.random.default_rng(seed)
+    bits = np.concatenate([r.integers(1, 0x7BFF, size=n_amax - 6, endpoint=True),
+                           [0x0001, 0x0400, 0x3C00, 0x4700, 0x7BFF, 0x0000]]).astype(np.uint16)
+    amax = bits.view(np.float16)
+    _, Ma, Ea = xr.decode_fp16(amax)
+    # fl32(1e-12): 1e-12 = 2^-12 / 5^12, rounded once
+    Qe, Te = xr.round_to(*xr.divide(np.array([1]), np.array([-12]), 5 ** 12), xr.FP32)
+    eps = xr.to_float64(Qe, Te)[0]
+    assert eps == float(np.float32(1e-12))  # the literal as a float32 constant takes the same value
+    for p in range(1, 101):
+        Qa, Ta = xr.round_to(*xr.divide(np.array([p]), np.array([0]), 100), xr.FP32)
+        Mp, Ep = xr.multiply(Ma, Ea, Qa[0], Ta[0])
+        Qm, Tm = xr.round_to(Mp, Ep, False, xr.FP32)
+        small = xr.to_float64(Qm, Tm) < eps
+        Qm = np.where(small, Qe[0], Qm)
+        Tm = np.where(small, Te[0], Tm)
+        Q32, T32 = xr.round_to(*xr.divide(Qm, Tm, 7), xr.FP32)
+        Q16, T16 = xr.round_to(Q32, T32, False, xr.FP16)
+        got = o.clip_scale_fp16(amax, p).astype(np.float64)
+        exp = xr.to_float64(Q16, T16)
+        assert np.array_equal(got, exp), (p, np.flatnonzero(got != exp)[:5])
 
 
 def pin_clip_never_worse_than_rtn(seed=24):

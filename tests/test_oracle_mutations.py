@@ -159,6 +159,25 @@ def _asym_levels16(monkeypatch):
     monkeypatch.setattr(oracle.rtn, "asym_scale_fp16", lambda mn, mx, levels=15: orig(mn, mx, 16))
 
 
+def _asym_range_fp16(monkeypatch):
+    def sc(mn16, mx16, levels=15):                                   # range formed in float16 (an fp16 tensor's max - min)
+        with np.errstate(over="ignore"):
+            rng16 = (np.asarray(mx16, dtype=np.float16) - np.asarray(mn16, dtype=np.float16)).astype(np.float16)
+            return (rng16.astype(np.float32) / np.float32(levels)).astype(np.float16)
+
+    monkeypatch.setattr(oracle.rtn, "asym_scale_fp16", sc)
+    monkeypatch.setattr(oracle, "asym_scale_fp16", sc)
+
+
+def _clip_scale_one_rounding(monkeypatch):
+    def sc(amax16, percent):                                         # p/100 * amax / 7 in float64, one rounding
+        a = np.maximum(np.asarray(amax16, dtype=np.float16).astype(np.float64) * percent / 100.0, 1e-12)
+        return (a / 7.0).astype(np.float16)
+
+    monkeypatch.setattr(oracle.clip, "clip_scale_fp16", sc)
+    monkeypatch.setattr(oracle, "clip_scale_fp16", sc)
+
+
 def _clip_ties_to_smaller(monkeypatch):
     orig = oracle.clip.clip_errors
 
@@ -357,8 +376,8 @@ def _kv_bytes_no_factor_two(monkeypatch):
 MUTATIONS = [
     _scale_div8, _scale_two_alpha_over_15, _truncate, _half_away, _fp16_quotient, _nibbles_swapped,
     _device_nibble_order, _device_lane_order, _dequant_wrong_group, _gemm_rows_reversed,
-    _gemm_fp16_accumulate, _asym_zero_sign, _asym_dequant_plus, _asym_levels16,
-    _clip_ties_to_smaller, _clip_qmin8, _clip_error_on_codes, _clip_without_100,
+    _gemm_fp16_accumulate, _asym_zero_sign, _asym_dequant_plus, _asym_levels16, _asym_range_fp16,
+    _clip_ties_to_smaller, _clip_scale_one_rounding, _clip_qmin8, _clip_error_on_codes, _clip_without_100,
     _w8_div128, _w8_clamp_m128, _w8_truncate, _w8_half_away, _w8_fp16_quotient, _w8_scale_per_column,
     _w8_layout_h_m_swapped, _w8_offset127, _w8_dequant_rows_shifted,
     _actorder_ascending, _actorder_gidx_inverted, _actorder_ties_reversed, _actorder_dequant_by_position,
