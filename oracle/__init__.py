@@ -60,7 +60,7 @@ from .layout import (  # noqa: F401
     groupwise_to_device,
     groupwise_from_device,
 )
-from .gemm import gemm_ref, gemm_ref_rows, to_fp16  # noqa: F401
+from .gemm import gemm_ref, gemm_ref_rows  # noqa: F401
 from .clip import clip_scale_fp16, clip_codes, clip_errors, quantize_sym_clip  # noqa: F401
 from .actorder import actorder_order, actorder_gidx, quantize_sym_actorder, dequant_gidx, gemm_gidx_rows  # noqa: F401
 from .kv import quantize_kv_int4, pack_kv_int4, dequant_kv_int4, kv_bytes_per_token  # noqa: F401

@@ -10,9 +10,6 @@ activations stay 16-bit ([ARG] section 二.3). The result here is that
 definition computed in float64: the dequantized weights are exact in float64
 and the only rounding is the float64 accumulation, far below the float16
 output's resolution.
-
-The kernels return float16; ``to_fp16`` rounds a float64 result to float16
-(round-to-nearest-even) for reporting.
 """
 
 from __future__ import annotations
@@ -44,8 +41,3 @@ def gemm_ref_rows(x16, q, s16, g: int, rows, z=None) -> np.ndarray:
     else:
         w_hat = dequant_asym(qr, sr, np.asarray(z)[rows], g)
     return gemm_ref(x16, w_hat)
-
-
-def to_fp16(y) -> np.ndarray:
-    """Round float64 results to float16 (RNE)."""
-    return np.asarray(y, dtype=np.float64).astype(np.float16)

@@ -233,15 +233,17 @@ def pin_noise_model(N=1024, K=4096, seed=0, groups=(4096, 512, 128, 32)):
     """
     o = _orc()
     W = synth.weight(N, K, seed=seed)
-    prev = None
+    mse_of = {}
     for g in groups:
         q, s16 = o.quantize_sym(W, g)
         mse = o.quant_mse(W, o.dequant_sym(q, s16, g))
         model = float(np.mean(s16.astype(np.float64) ** 2)) / 12 * (g - 1) / g
         assert abs(mse / model - 1) < 0.005, (g, mse, model)
-        if prev is not None:
-            assert mse < prev, (g, mse, prev)
-        prev = mse
+        mse_of[g] = mse
+    # the ordering the page prints (its magnitudes are not reproducible; the model above fixes them)
+    printed = {int(k): v for k, v in _golden("ybb_mse_by_group.json")["printed_mse"].items()}
+    by_printed = sorted(printed, key=lambda g: -printed[g])
+    assert [g for g in sorted(mse_of, key=lambda g: -mse_of[g]) if g in printed] == by_printed, mse_of
 
 
 def pin_asym_exact_grid(seed=7):

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -91,21 +92,6 @@ size_t lds_per_block() {
     lim = (size_t)v;
   cache[dev] = lim;
   return lim;
-}
-
-// Compute units of the current device (256 if it cannot be queried).
-int device_cu_count() {
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
-  int v = 0;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
-  cache[dev] = v;
-  return v;
 }
 
 // LDS of one GEMV workgroup with a single unit of work (q4_gemm.hip, GemvLds): x
@@ -220,6 +206,48 @@ size_t splits_workspace(const q4::GemmArgs& a) {
 size_t perm_x_bytes(int64_t B, int64_t in) { return (size_t)round_up(B * in * 2, 256); }
 
 }  // namespace
+
+namespace q4 {
+
+namespace {
+int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  return dev;
+}
+std::mutex g_dev_mu;
+std::map<int, int> g_cus;                                              // device -> CUs
+std::map<std::tuple<const void*, int, size_t, int>, int> g_resident;  // (kernel, block, lds, device) -> per CU
+}  // namespace
+
+int device_cu_count_cached() {
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
+  g_cus[dev] = v;
+  return v;
+}
+
+int resident_per_cu(const void* fn, int block, size_t lds) {
+  const auto key = std::make_tuple(fn, block, lds, current_device());
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = g_resident.find(key);
+    if (it != g_resident.end()) return it->second;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess || nb < 1) nb = 1;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  g_resident[key] = nb;
+  return nb;
+}
+
+int resident_grid(const void* fn, int block) { return resident_per_cu(fn, block, 0) * device_cu_count_cached(); }
+
+}  // namespace q4
 
 extern "C" {
 
@@ -623,7 +651,10 @@ static q4_status check_kv(int64_t bh, int64_t n, int64_t head_dim, int32_t group
                 (long long)pos, (long long)max_seq);
   if (pos + n > max_seq)
     return fail(Q4_ERR_SHAPE, "pos + n = %lld exceeds max_seq = %lld", (long long)(pos + n), (long long)max_seq);
-  if (bh * max_seq * head_dim >= (int64_t(1) << 46)) return fail(Q4_ERR_SHAPE, "cache too large");
+  int64_t cells = 0, elems = 0;  // each factor is below 2^31, but their product may not fit 64 bits
+  if (__builtin_mul_overflow(bh, max_seq, &cells) || __builtin_mul_overflow(cells, head_dim, &elems) ||
+      elems >= (int64_t(1) << 46))
+    return fail(Q4_ERR_SHAPE, "cache too large");
   return Q4_OK;
 }
 
@@ -658,7 +689,7 @@ q4_status q4_read_probe(const void* buf, size_t bytes, void* sink, void* stream)
   if (!buf || !sink) return fail(Q4_ERR_NULL, "buf and sink must be non-NULL");
   if (bytes == 0 || bytes % 8192 != 0) return fail(Q4_ERR_SHAPE, "bytes=%zu must be a positive multiple of 8192", bytes);
   if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(Q4_ERR_ALIGN, "buf needs 16-byte, sink 4-byte alignment");
-  return hip_status(q4::launch_read_probe(buf, (int64_t)(bytes / 8192), sink, device_cu_count(),
+  return hip_status(q4::launch_read_probe(buf, (int64_t)(bytes / 8192), sink, q4::device_cu_count_cached(),
                                           static_cast<hipStream_t>(stream)), "read probe launch");
 }
 

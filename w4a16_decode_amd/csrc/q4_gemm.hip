@@ -22,9 +22,6 @@
 //    GEMM: 2 to 8 column tiles of 16 batch rows per workgroup, staged through LDS
 //    and shared by its 8 (or 4) wavefronts, each owning whole row tiles.
 #include <algorithm>
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "q4_device.h"
 #include "q4_internal.h"
@@ -486,7 +483,7 @@ void launch_reduce_splits(const float* ws, int KS, int64_t BN, uint16_t* y, hipS
 // whole activation slice, and x is read from L2 in small pieces spread over the
 // kernel. Units are at least P - 1 blocks long, so a wavefront never has the x of
 // more than one unit waiting in registers.
-constexpr int kUnitBlocks = 8;
+constexpr int kUnitBlocks = kStreamUnitBlocks;
 constexpr int kUnitXStride = kUnitBlocks * kSuperK + 8;  // halfs per batch row of a unit's x in LDS
 
 // LDS of one streaming workgroup, in bytes (shared with the host-side sizing).
@@ -764,36 +761,6 @@ void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __re
   }
 }
 
-// Resident workgroups per CU for a kernel / block / LDS combination, and the CU
-// count of the current device; both are fixed for a process, so they are looked
-// up once and remembered.
-int resident_per_cu(const void* fn, int block, size_t lds) {
-  static std::mutex mu;
-  static std::map<std::tuple<const void*, int, size_t>, int> cache;
-  std::lock_guard<std::mutex> lk(mu);
-  auto key = std::make_tuple(fn, block, lds);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess || nb < 1) nb = 1;
-  cache[key] = nb;
-  return nb;
-}
-
-int device_cus() {
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  cache[dev] = cus;
-  return cus;
-}
-
 template <int R, int GSUB, bool ASYM, int XCH, bool Q8 = false>
 hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   // ring stages per row-tile count: INT4 with one row tile, two bursts of 4
@@ -814,7 +781,7 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   // Persistent grid: as many workgroups as stay resident, the row blocks spread
   // evenly over them; more workgroups only if one row block per chunk would not
   // fit the LDS limit.
-  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, base + unit_bytes) * device_cus();
+  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, base + unit_bytes) * device_cu_count_cached();
   int64_t per_split = std::max<int64_t>(1, std::min<int64_t>(nRB, resident / KS));
   if (a.grid_limit > 0) per_split = std::min<int64_t>(per_split, std::max(1, a.grid_limit / KS));
   int n_rb = (int)((nRB + per_split - 1) / per_split);
@@ -881,7 +848,7 @@ hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, 0).total;
   const size_t lim = std::max(a.lds_limit, base + unit_bytes * CH);
-  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, base + unit_bytes * CH) * device_cus();
+  const int64_t resident = (int64_t)resident_per_cu(fn, W * kWave, base + unit_bytes * CH) * device_cu_count_cached();
   int64_t grid = std::max<int64_t>(1, std::min<int64_t>(nRB, resident));
   if (a.grid_limit > 0) grid = std::min<int64_t>(grid, a.grid_limit);
   int n_rb = (int)((nRB + grid - 1) / grid);
@@ -914,15 +881,6 @@ template <int R>
 hipError_t launch_gemv_stream_a(const GemmArgs& a, hipStream_t stream) {
   return a.asym ? launch_gemv_stream_g<R, true>(a, stream) : launch_gemv_stream_g<R, false>(a, stream);
 }
-
-}  // namespace
-
-bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
-  const int S = Kp / kSuperK;
-  return B >= 1 && B <= 3 && k_splits == 1 && rows_per_wave == 2 && S % kUnitBlocks == 0;
-}
-
-namespace {
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
   if (a.q8) {

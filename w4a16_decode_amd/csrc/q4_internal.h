@@ -88,12 +88,21 @@ hipError_t launch_w8_from_canonical(const W8Args& a, hipStream_t stream);
 hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Blocks of 128 channels in one unit of the streaming GEMV.
+constexpr int kStreamUnitBlocks = 8;
+
 // Whether the GEMV for this shape streams x per unit (B <= 3, one split, two row
 // tiles per wavefront, a multiple of 1024 channels) instead of staging the whole slice.
-bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits);
-// Compute units of the current device, and the workgroups of `block` threads of
-// kernel fn it holds at once (both cached, lock-guarded).
+inline bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
+  const int S = Kp / 128;
+  return B >= 1 && B <= 3 && k_splits == 1 && rows_per_wave == 2 && S % kStreamUnitBlocks == 0;
+}
+// Facts of the current device, each looked up once per device and kept in one
+// lock-guarded cache (q4_api.cpp): its compute units, the workgroups of `block`
+// threads with `lds` bytes of dynamic LDS of kernel fn one CU holds at once, and
+// the same times the CU count for kernels without dynamic LDS.
 int device_cu_count_cached();
+int resident_per_cu(const void* fn, int block, size_t lds);
 int resident_grid(const void* fn, int block);
 
 }  // namespace q4

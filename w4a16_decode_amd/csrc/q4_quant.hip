@@ -15,51 +15,12 @@
 // the IEEE float32 one); it is taken from one reciprocal per scale and a multiply
 // per weight (q4_rtn.h).
 #include <algorithm>
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "q4_device.h"
 #include "q4_internal.h"
 #include "q4_rtn.h"
 
 namespace q4 {
-
-// Compute units of the current device (cached per device).
-int device_cu_count_cached() {
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  cache[dev] = cus;
-  return cus;
-}
-
-// Workgroups of `block` threads of kernel fn that the current device holds at once
-// (cached per kernel and device).
-int resident_grid(const void* fn, int block) {
-  static std::mutex mu;
-  static std::map<std::tuple<const void*, int, int>, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  const auto key = std::make_tuple(fn, block, dev);
-  {
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-  }
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess || nb < 1) nb = 1;
-  const int grid = nb * device_cu_count_cached();
-  std::lock_guard<std::mutex> lk(mu);
-  cache[key] = grid;
-  return grid;
-}
 
 namespace {
 
@@ -127,10 +88,10 @@ __device__ __forceinline__ float wave_min4(float a) {
 
 __device__ __forceinline__ uint16_t half_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
-// Symmetric scale of a group from its amax (float32 IEEE divide, RNE to float16).
-// fp16(fp32(amax) / 7) for a float16-valued amax: the product with the float32 constant
-// fl(1/7) rounds to the same float16 for every positive float16 amax (checked for all
-// of them on the host), so no divide is needed
+// Symmetric scale of a group from its amax: fp16(fp32(amax) / 7), RNE to float16, formed
+// as the product with the float32 constant fl(1/7), which rounds to the same float16 as
+// the IEEE quotient for every positive float16 amax (checked for all of them on the
+// host), so no divide is needed
 __device__ __forceinline__ _Float16 sym_scale(float amax) { return (_Float16)(fmaxf(amax, 1e-12f) * (1.0f / 7.0f)); }
 
 // r = rtn_recip(s): 0 for s == 0, which gives the code of q = 0 (and z = 0)
