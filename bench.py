@@ -22,8 +22,8 @@ The same line carries:
                 throughput and the B = 1 GEMV on heavy-tailed 14336x4096 weights.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
-Profiling helpers: --only-kernel {gate_up,down,qkv,o} [--reps N] runs just that
-GEMV kind of a few 70B layers; --only-batch B [--reps N] runs the product on one
+Profiling helpers: --only-kernel {gate_up,down,qkv,o} [--batch B] [--reps N] runs just
+that GEMV kind of a few 70B layers; --only-batch B [--reps N] runs the product on one
 28672x8192 matrix at batch B; --only-quantize, --only-w8, --only-actorder, --only-kv
 run just that extra measurement; --copy-calibration runs a 256 MiB device copy.
 """
@@ -517,21 +517,21 @@ def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) 
             "dequant_s": t_deq, "matmul_s": t_mm, "quantize_s": t_q, "quantize_bytes": q_bytes}
 
 
-def only_kernel(kind: str, reps: int, layers: int, dev, group: int):
-    """Run just one GEMV kind of a few 70B layers, for counter collection."""
+def only_kernel(kind: str, reps: int, layers: int, dev, group: int, batch: int = 1):
+    """Run just one GEMV kind of a few 70B layers at `batch` rows, for counter collection."""
     import torch
 
     import synth
     import w4a16_decode_amd as q4
 
     model = build_model(synth.LLAMA3_70B, layers, seed=3, group=group, device=dev)
-    sweep = Sweep(model, 1, seed=3, device=dev)
+    sweep = Sweep(model, batch, seed=3, device=dev)
     picked = [(x, qw, y) for name, x, qw, y in sweep.launches() if KIND_OF[name] == kind]
     for _ in range(reps):
         for x, qw, y in picked:
             q4.gemm(x, qw, out=y, workspace=sweep.ws)
     torch.cuda.synchronize()
-    log(f"[bench] ran {kind} x {reps * len(picked)}")
+    log(f"[bench] ran {kind} B={batch} x {reps * len(picked)}")
 
 
 def only_batch(B: int, reps: int, dev, group: int):
@@ -573,6 +573,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-kernel", choices=["gate_up", "down", "qkv", "o"])
     ap.add_argument("--only-batch", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=1, help="batch rows for --only-kernel")
     ap.add_argument("--only-w8", action="store_true", help="only the W8A16 layer measurement")
     ap.add_argument("--only-actorder", action="store_true", help="only the act-order layer measurement")
     ap.add_argument("--only-kv", action="store_true", help="only the INT4 KV-cache measurement")
@@ -600,7 +601,7 @@ def main(argv=None):
         copy_calibration(dev)
         return 0
     if args.only_kernel:
-        only_kernel(args.only_kernel, args.reps, min(args.layers, 4), dev, group)
+        only_kernel(args.only_kernel, args.reps, min(args.layers, 4), dev, group, args.batch)
         return 0
     if args.only_batch:
         only_batch(args.only_batch, args.reps, dev, group)
