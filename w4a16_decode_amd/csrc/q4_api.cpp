@@ -100,7 +100,7 @@ size_t lds_per_block() {
 size_t gemv_lds(int B, int S, int KS, int R, int group, bool asym) {
   const size_t nsb = (size_t)((S + KS - 1) / KS);
   const size_t gsub = group >= 128 ? 1 : (size_t)(128 / group);
-  const size_t x = (((size_t)B * (nsb * 128 + 8) + 128) * 2 + 15) & ~(size_t)15;
+  const size_t x = (((size_t)B * (nsb * 128 + q4::kGemmRowPad) + 128) * 2 + 15) & ~(size_t)15;
   const size_t beta = asym ? 0 : ((size_t)B * nsb * gsub + 1 + 3) / 4 * 4 * sizeof(float);
   return x + beta + (size_t)R * 16 * B * 4 + 16;
 }
@@ -116,10 +116,8 @@ bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, siz
   return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
 }
 
-// LDS of one skinny-GEMM workgroup: two activation tiles of col_tiles * 16 rows x
-// (16 / col_tiles) * 128 channels, each row padded by 16 bytes (mfma_chunk_blocks in
-// q4_gemm.hip).
-size_t mfma_lds(int col_tiles) { return (size_t)2 * col_tiles * 16 * ((16 / col_tiles) * 128 + 8) * 2; }
+// LDS of one skinny-GEMM workgroup (q4_internal.h).
+size_t mfma_lds(int col_tiles) { return q4::mfma_lds_bytes(col_tiles); }
 
 // Skinny GEMM launch shapes: R x CT accumulator tiles and one partial tile per
 // group of a 128-channel block must fit the registers, the two activation tiles

@@ -75,13 +75,12 @@ struct WStage {
   bool last; // last block of its unit (uniform)
 };
 
-constexpr int kXChunksPerThread = 8;  // x slice <= 8 * 16 B * blockDim (XCH is 2, 4 or 8)
 
 // LDS layout of one GEMV workgroup, in bytes (shared with the host-side sizing).
 struct GemvLds {
   size_t x, beta, part, total;
   __host__ __device__ GemvLds(int B, int nsb, int GSUB, bool bias, int R, int units) {
-    x = ((((size_t)B * (nsb * kSuperK + 8) + kSuperK) * 2) + 15) & ~(size_t)15;  // x rows + zero row
+    x = ((((size_t)B * (nsb * kSuperK + kGemmRowPad) + kSuperK) * 2) + 15) & ~(size_t)15;  // x rows + zero row
     beta = bias ? (((size_t)B * nsb * GSUB + 1 + 3) / 4 * 4) * 4 : 0;            // per-unit biases + a zero
     part = (size_t)units * R * 16 * B * 4;  // partial sums of every unit
     total = x + beta + part + 16;           // + the unit counter
@@ -141,7 +140,7 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
   const int n_rb = rb_first < nRB ? (nRB - 1 - rb_first) / rb_stride + 1 : 0;
   const int n_units = n_rb * CH;
   const int KR = nsb * kSuperK;
-  const int xstride = KR + 8;  // halfs per x row in LDS (16-byte pad against bank conflicts)
+  const int xstride = KR + kGemmRowPad;  // halfs per x row in LDS (32-byte pad: conflict-free operand reads)
   const int nunits = nsb * GSUB;
   const GemvLds lay(B, nsb, GSUB, BIAS, R, n_units);
   uint16_t* xl = reinterpret_cast<uint16_t*>(smem);      // x (x/16 at the scaled elements when BIAS)
@@ -484,7 +483,7 @@ void launch_reduce_splits(const float* ws, int KS, int64_t BN, uint16_t* y, hipS
 // kernel. Units are at least P - 1 blocks long, so a wavefront never has the x of
 // more than one unit waiting in registers.
 constexpr int kUnitBlocks = kStreamUnitBlocks;
-constexpr int kUnitXStride = kUnitBlocks * kSuperK + 8;  // halfs per batch row of a unit's x in LDS
+constexpr int kUnitXStride = kUnitBlocks * kSuperK + kGemmRowPad;  // halfs per batch row of a unit's x in LDS
 
 // LDS of one streaming workgroup, in bytes (shared with the host-side sizing).
 struct GemvStreamLds {
@@ -933,7 +932,7 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
   constexpr int MPG = 4 / GSUB;
   constexpr int XROWS = CT * 16;
   constexpr int KC = NB * kSuperK;           // channels per chunk
-  constexpr int XSTR = KC + 8;               // halfs per LDS row (16-byte pad against bank conflicts)
+  constexpr int XSTR = KC + kGemmRowPad;     // halfs per LDS row (32-byte pad: conflict-free B reads)
   constexpr int C8 = KC / 8;                 // 16-byte pieces per row of a chunk
   constexpr int NT = WV * 64;                // threads
   constexpr int XCH = XROWS * C8 / NT;       // pieces of one chunk's tile per thread
@@ -1109,7 +1108,7 @@ hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
   const int col_tiles = (a.B + 15) / 16;
   const int KS = a.k_splits;
   dim3 grid((T + WV * RT - 1) / (WV * RT), (col_tiles + CT - 1) / CT, KS);
-  const size_t lds = (size_t)2 * CT * 16 * (NB * kSuperK + 8) * 2;
+  const size_t lds = mfma_lds_bytes(CT);
   hipLaunchKernelGGL((gemm_mfma_kernel<RT, CT, GSUB, ASYM, NB, WV, Q8>), grid, dim3(WV * 64), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,

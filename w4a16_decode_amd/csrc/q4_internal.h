@@ -91,6 +91,18 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // Blocks of 128 channels in one unit of the streaming GEMV.
 constexpr int kStreamUnitBlocks = 8;
 
+// Activation rows in LDS (GEMV slices and units, skinny-GEMM tiles) are padded by 16
+// halfs (32 bytes): the 16 lanes of a B-operand read (16 rows, 16 bytes each) then
+// hit distinct banks; a 16-byte pad leaves 2-way conflicts, which halved the LDS
+// read rate in a plain read loop.
+constexpr int kGemmRowPad = 16;
+
+// Skinny GEMM LDS: two activation tiles of col_tiles * 16 batch rows by
+// (16 / col_tiles) * 128 channels, padded rows. One workgroup per CU.
+constexpr size_t mfma_lds_bytes(int col_tiles) {
+  return (size_t)2 * col_tiles * 16 * ((16 / col_tiles) * 128 + kGemmRowPad) * 2;
+}
+
 // Whether the GEMV for this shape streams x per unit (B <= 3, one split, two row
 // tiles per wavefront, a multiple of 1024 channels) instead of staging the whole slice.
 inline bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
