@@ -153,6 +153,21 @@ q4_status q4_gemm(const void* x, int64_t B, const void* packed, const void* scal
                   int64_t out, int64_t in, int32_t group, void* y,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* q4_gemm for callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture that must not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation). Same product, same kernels and same results as
+ * q4_gemm; the split partial sums that q4_gemm keeps in the caller's workspace go to
+ * a library-owned device array of Q4_NOALLOC_SCRATCH_BYTES instead, one per GPU,
+ * reserved when the library is loaded and held until the process ends. The call
+ * allocates nothing. Shapes needing more than that (q4_workspace_bytes(B, out, in,
+ * group) > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ERR_WORKSPACE. The array is shared by
+ * every q4_gemm_noalloc call on a GPU and keeps the last call's contents (each call
+ * overwrites what it reads): calls that overlap on one GPU, on different streams or
+ * host threads, race and must be serialized by the caller. */
+#define Q4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+q4_status q4_gemm_noalloc(const void* x, int64_t B, const void* packed, const void* scales,
+                          int64_t out, int64_t in, int32_t group, void* y, void* stream);
+
 /* As q4_gemm for asymmetric weights: the inner sum uses (q - z[n][j]). */
 q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void* scales,
                        const void* zeros, int64_t out, int64_t in, int32_t group, void* y,

@@ -43,6 +43,12 @@ hipError_t launch_read_probe(const void*, int64_t, void*, int, hipStream_t) {
   ++g_launches;
   return g_launch_result;
 }
+int g_scratch_lookups = 0;
+hipError_t noalloc_scratch(void** out) {
+  ++g_scratch_lookups;
+  *out = reinterpret_cast<void*>(0x7000000);
+  return hipSuccess;
+}
 }  // namespace q4
 
 extern "C" {
@@ -130,6 +136,15 @@ int main() {
     const size_t w8 = q8_workspace_bytes(B, N, K);
     VALID(q8_gemm(P, B, P, P, N, K, P, P, w8, nullptr), 1);
   }
+  // the no-allocation product: the library scratch stands in for the workspace
+  q4::g_scratch_lookups = 0;
+  VALID(q4_gemm_noalloc(P, 1, P, P, 4096, 4096, 128, P, nullptr), 1);
+  EXPECT(q4::g_scratch_lookups == 0, "no scratch lookup where no split needs it");
+  VALID(q4_gemm_noalloc(P, 8, P, P, 8192, 28672, 128, P, nullptr), 1);
+  EXPECT(q4::g_scratch_lookups > 0, "scratch looked up for a split product");
+  EXPECT(q4_workspace_bytes(16, 65536, 262144, 128) > Q4_NOALLOC_SCRATCH_BYTES, "a split beyond the scratch");
+  CHECK_CALL(q4_gemm_noalloc(P, 16, P, P, 65536, 262144, 128, P, nullptr), Q4_ERR_WORKSPACE, 0);
+  CHECK_CALL(q4_gemm_noalloc(nullptr, 4, P, P, 8192, 28672, 128, P, nullptr), Q4_ERR_NULL, 0);
   CHECK_CALL(q4_gemm(P, 0, nullptr, nullptr, 16, 128, 128, nullptr, nullptr, 0, nullptr), Q4_OK, 0);
   CHECK_CALL(q4_gemm(P, -1, P, P, 16, 128, 128, P, nullptr, 0, nullptr), Q4_ERR_SHAPE, 0);
   CHECK_CALL(q4_gemm(P, 1, P, P, 16, 128, 128, nullptr, nullptr, 0, nullptr), Q4_ERR_NULL, 0);

@@ -36,6 +36,7 @@ SIGNATURES = {
     "q4_quantize_pack_clip": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P]),
     "q4_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
     "q4_gemm_asym": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
+    "q4_gemm_noalloc": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I64, _I32, _P, _P]),
     "q4_gemm_config": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _P, _I32, _I32, _I32, _I32, _P, _SZ,
                                       _P]),
     "q4_to_canonical": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I32, _P, _P, _P, _P]),

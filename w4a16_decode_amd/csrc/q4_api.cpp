@@ -37,6 +37,7 @@ q4_status ok() {
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+static_assert(Q4_NOALLOC_SCRATCH_BYTES == q4::kNoAllocScratchBytes, "q4.h and the scratch array agree");
 
 bool group_ok(int32_t g) { return g == 32 || g == 64 || (g >= 128 && g % 128 == 0); }
 
@@ -323,7 +324,8 @@ q4_status q4_quantize_pack_clip(const void* W, int64_t out, int64_t in, int32_t 
 static q4_status gemm_common(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,
                              bool asym, int64_t out, int64_t in, int32_t group, void* y, int rows_per_wave,
                              int waves_per_group, int k_splits, int col_tiles, void* workspace,
-                             size_t workspace_bytes, void* stream, const int32_t* perm = nullptr) {
+                             size_t workspace_bytes, void* stream, const int32_t* perm = nullptr,
+                             bool noalloc = false) {
   if (B < 0 || B >= kMaxDim) return fail(Q4_ERR_SHAPE, "B=%lld out of range", (long long)B);
   Dims d;
   q4_status st = check_dims(out, in, group, &d);
@@ -378,6 +380,19 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
     a.k_splits = k_splits;
   }
   const size_t need = splits_workspace(a) + (perm ? perm_x_bytes(B, in) : 0);
+  if (noalloc) {
+    // the library's own scratch array stands in for the workspace
+    if (need > q4::kNoAllocScratchBytes)
+      return fail(Q4_ERR_WORKSPACE, "this shape needs %zu bytes of scratch, more than the %zu q4_gemm_noalloc holds",
+                  need, q4::kNoAllocScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      q4_status st2 = hip_status(q4::noalloc_scratch(&workspace), "scratch address lookup");
+      if (st2 != Q4_OK) return st2;
+      workspace_bytes = q4::kNoAllocScratchBytes;
+    }
+  }
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(Q4_ERR_WORKSPACE, "this shape needs %zu bytes of workspace (q4_workspace_bytes%s), got %zu", need,
@@ -392,6 +407,12 @@ q4_status q4_gemm(const void* x, int64_t B, const void* packed, const void* scal
                   int32_t group, void* y, void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, 0, 0, workspace, workspace_bytes,
                      stream);
+}
+
+q4_status q4_gemm_noalloc(const void* x, int64_t B, const void* packed, const void* scales, int64_t out, int64_t in,
+                          int32_t group, void* y, void* stream) {
+  return gemm_common(x, B, packed, scales, nullptr, false, out, in, group, y, 0, 0, 0, 0, nullptr, 0, stream, nullptr,
+                     true);
 }
 
 q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void* scales, const void* zeros,

@@ -23,6 +23,9 @@
 //    and shared by its 8 (or 4) wavefronts, each owning whole row tiles.
 #include <algorithm>
 
+#include <map>
+#include <mutex>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -1180,6 +1183,31 @@ __global__ void gather_cols_kernel(const uint16_t* __restrict__ x, int B, int K,
         make_uint4(at(p0.x) | at(p0.y) << 16, at(p0.z) | at(p0.w) << 16, at(p1.x) | at(p1.y) << 16,
                    at(p1.z) | at(p1.w) << 16);
   }
+}
+
+// Library-owned device scratch for q4_gemm_noalloc (callers that cannot allocate):
+// the split partial sums that q4_gemm keeps in the caller's workspace. Each GPU the
+// library runs on holds its own copy until the process ends. In host code `scratch`
+// names a host-side stand-in, so its device address is looked up once per device
+// and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // on the current device
+    if (e != hipSuccess) return e;
+    it = ptrs.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {

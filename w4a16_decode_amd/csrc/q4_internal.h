@@ -88,6 +88,10 @@ hipError_t launch_w8_from_canonical(const W8Args& a, hipStream_t stream);
 hipError_t launch_to_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_from_canonical(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Device address (on the current device) of the library-owned scratch array that
+// q4_gemm_noalloc uses in place of a workspace; looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** out);
 // Blocks of 128 channels in one unit of the streaming GEMV.
 constexpr int kStreamUnitBlocks = 8;
 

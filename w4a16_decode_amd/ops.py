@@ -193,6 +193,18 @@ def gemm(x, qw: QuantizedWeight, out=None, workspace=None):
     return out
 
 
+def gemm_noalloc(x, qw: QuantizedWeight, out=None):
+    """q4_gemm_noalloc: q4_gemm with the library's own device scratch in place of a
+    workspace (symmetric weights). Allocates nothing when `out` is given; calls that
+    overlap on one GPU race on that scratch."""
+    if qw.asym:
+        raise ValueError("q4_gemm_noalloc takes symmetric weights")
+    B, out = _prep_gemm(x, qw, out)
+    _check(_lib.load().q4_gemm_noalloc(x.data_ptr(), B, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.out_features,
+                                       qw.in_features, qw.group, out.data_ptr(), _stream(x)))
+    return out
+
+
 def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int, k_splits: int = 1,
                 col_tiles: int | None = None, out=None, workspace=None):
     """q4_gemm_config: q4_gemm with an explicit launch shape (tuning).
