@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "W4A16 GEMV effective HBM GB/s & % of peak (B=1); us/layer vs B"
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_gate_up_70b_b1_traffic.txt")
+STATS_PROFILE = os.path.join(ROOT, "profiles", "gemv_70b_sweep_b1_kernel_stats.txt")
 KIND_OF = {"q_proj+k_proj+v_proj": "qkv", "o_proj": "o", "gate_proj+up_proj": "gate_up", "down_proj": "down"}
 
 
@@ -197,23 +198,29 @@ def measured_read_gbs(dev) -> float:
     return nbytes / t / 1e9
 
 
-def recorded_traffic():
-    """Traffic per launch from profiles/, only if taken on the current kernel sources."""
+def recorded_value(path: str, key: str):
+    """A `key: value` line of a summary under profiles/, only if that summary was taken
+    on the current kernel sources (its kernel_fingerprint line matches)."""
     from w4a16_decode_amd import profiling
 
-    if not os.path.exists(TRAFFIC_PROFILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_PROFILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("kernel_fingerprint") != profiling.kernel_fingerprint():
         return None
     try:
-        return float(vals["bytes"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic():
+    """Traffic per launch from profiles/, only if taken on the current kernel sources."""
+    return recorded_value(TRAFFIC_PROFILE, "bytes")
 
 
 def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
@@ -286,15 +293,8 @@ def extras_quantize(dev):
         for asym in (False, True):
             qws = [q4.quantize_pack(W, g, asym=asym) for W in Ws]
             torch.cuda.synchronize()
-            a, b = events()
-            a.record()
-            reps = 3
-            for _ in range(reps):
-                for W in Ws:
-                    q4.quantize_pack(W, g, asym=asym)
-            b.record()
-            torch.cuda.synchronize()
-            tq = a.elapsed_time(b) / 1e3 / (reps * len(Ws))
+            # the quantizer's launches captured in a HIP graph (into the buffers of qws)
+            tq = graph_time(lambda: [q4.quantize_pack_into(W, qw) for W, qw in zip(Ws, qws)], 3) / len(Ws)
             ws = torch.empty(max(16, q4.workspace_bytes(1, N, K, g)), dtype=torch.uint8, device=dev)
             tg = graph_time(lambda: [q4.gemm(x, qw, out=y, workspace=ws) for qw in qws]) / len(qws)
             qb = perfmodel.quantize_bytes(N, K, g, asym)
@@ -305,14 +305,9 @@ def extras_quantize(dev):
             del qws
         # clipping search (alpha = 0.80 .. 1.00 of the group amax): time, and the weight
         # reconstruction error against RTN's (dequantized from the library's own codes)
-        torch.cuda.synchronize()
-        a, b = events()
-        a.record()
-        for W in Ws[:4]:
-            qc = q4.quantize_pack_clip(W, g, 80)
-        b.record()
-        torch.cuda.synchronize()
-        tc = a.elapsed_time(b) / 1e3 / 4
+        qcs = [q4.quantize_pack_clip(W, g, 80) for W in Ws[:4]]
+        tc = graph_time(lambda: [q4.quantize_pack_clip_into(W, qc, 80) for W, qc in zip(Ws[:4], qcs)], 2) / 4
+        qc = qcs[0]
         qr = q4.quantize_pack(base, g)
         mse = {}
         for name, qw in (("rtn", qr), ("clip", qc)):
@@ -470,7 +465,7 @@ def extras_kv(dev):
     return out
 
 
-def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) -> dict:
+def cpu_baseline(dev, group: int, target_s: float = 8.0, max_layers: int = 12) -> dict:
     """Oracle (numpy) W4A16 product on whole layers of the 70B sweep, until ~target_s of CPU time."""
     import numpy as np
     import torch
@@ -515,6 +510,59 @@ def cpu_baseline(dev, group: int, target_s: float = 10.0, max_layers: int = 12) 
         layers += 1
     return {"seconds": t_total, "bytes": total_bytes, "threads": threads, "layers": layers,
             "dequant_s": t_deq, "matmul_s": t_mm, "quantize_s": t_q, "quantize_bytes": q_bytes}
+
+
+def cpu_configs(dev, group: int) -> dict:
+    """The oracle on the other workloads, in full: the 4096x4096 layer at B=1, the 28672x8192
+    batch sweep (one float64 dequantization, then the matmul at every B) and the heavy-tailed
+    14336x4096 quantizer at g = 32/64/128, symmetric and asymmetric. Seconds and GB/s on the
+    same byte formulas as the GPU figures."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from w4a16_decode_amd import perfmodel
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    out = {}
+    W1 = synth.weight(4096, 4096, seed=0)
+    x1 = synth.activation(1, 4096, seed=0)
+    (q, s), tq = timed(lambda: oracle.quantize_sym(W1, group))
+    wh, td = timed(lambda: oracle.dequant_sym(q, s, group))
+    _, tm = timed(lambda: oracle.gemm_ref(x1, wh))
+    nb = perfmodel.gemm_read_bytes(1, 4096, 4096, group)
+    out["single_layer_4096_b1"] = {"quantize_s": round(tq, 3), "dequant_s": round(td, 3), "matmul_s": round(tm, 4),
+                                   "gemv_GBps": round(nb / (td + tm) / 1e9, 3)}
+    N, K = 28672, 8192
+    W4 = synth.device_weight(N, K, seed=4, layer=0, matrix=0, device=dev).cpu().numpy()
+    (q, s), tq = timed(lambda: oracle.quantize_sym(W4, group))
+    del W4
+    wh, td = timed(lambda: oracle.dequant_sym(q, s, group))
+    del q, s
+    per_b = {}
+    for B in (1, 4, 16, 32, 64, 128, 256):
+        x = synth.activation(B, K, seed=4)
+        y, tm = timed(lambda: oracle.gemm_ref(x, wh))
+        assert np.all(np.isfinite(y))
+        per_b[str(B)] = {"matmul_s": round(tm, 4),
+                         "GBps_with_dequant": round(perfmodel.gemm_read_bytes(B, N, K, group) / (td + tm) / 1e9, 3),
+                         "GFLOPs_matmul": round(perfmodel.gemm_flops(B, N, K) / tm / 1e9, 1)}
+    del wh
+    out["batch_sweep_28672x8192"] = {"quantize_s": round(tq, 2), "dequant_s": round(td, 2), "per_B": per_b}
+    Wh, _ = synth.heavy_tailed_weight(14336, 4096, seed=5)
+    hq = {}
+    for g in (32, 64, 128):
+        for asym in (False, True):
+            _, tq = timed(lambda: oracle.quantize_asym(Wh, g) if asym else oracle.quantize_sym(Wh, g))
+            hq[f"g{g}_{'asym' if asym else 'sym'}"] = {
+                "quantize_s": round(tq, 3),
+                "quantize_GBps": round(perfmodel.quantize_bytes(14336, 4096, g, asym) / tq / 1e9, 3)}
+    out["heavy_tailed_14336x4096_quantize"] = hq
+    return out
 
 
 def only_kernel(kind: str, reps: int, layers: int, dev, group: int, batch: int = 1):
@@ -648,6 +696,11 @@ def main(argv=None):
                 "measured_read_GBps": round(read_gbs, 1), "frac_of_measured_read": round(k_gbs / read_gbs, 4),
                 "kernel": f"gemv_kernel, fused gate/up {qw0.out_features}x{qw0.in_features}, B=1, g=128",
                 "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes, "launches_timed": n_timed}
+    # the same kernel's average duration in the committed rocprofv3 kernel trace of this command
+    # (its summary under profiles/, while the kernel sources match): the two must agree
+    prof_us = recorded_value(STATS_PROFILE, "gate_up_avg_us_rocprof")
+    roofline["avg_us_rocprof"] = prof_us
+    roofline["rocprof_over_events"] = round(prof_us / (d_avg * 1e6), 4) if prof_us else None
 
     extras = {}
     if not args.no_extras:
@@ -672,6 +725,7 @@ def main(argv=None):
         s8.capture()
         t8 = s8.time_steps(args.steps, args.warmup)
         extras["sweep_8b_b1"] = {"ms_per_step": round(t8 * 1e3, 4), "GBps": round(s8.bytes_per_step() / t8 / 1e9, 1),
+                                 "pct_of_hbm_peak": round(s8.bytes_per_step() / t8 / 1e9 / perfmodel.HBM_PEAK_GBS, 4),
                                  "us_per_layer": round(t8 / 32 * 1e6, 2)}
         log(f"[bench] 8B sweep: {extras['sweep_8b_b1']}")
         del s8, m8
@@ -714,7 +768,11 @@ def main(argv=None):
                           "quantize_GBps": round(res["quantize_bytes"] / res["quantize_s"] / 1e9, 3),
                           "quantize_sample": "layer 0's fused q/k/v (10240x8192), numpy on 1 core",
                           "host_cpus": os.cpu_count()}}
-        log(f"[bench] cpu oracle: {cpu_gbs:.3f} GB/s over {res['seconds']:.1f}s ({res['layers']} layers)")
+        t0 = time.perf_counter()
+        cpu["stages"]["configs"] = cpu_configs(dev, group)
+        cpu["stages"]["configs_seconds"] = round(time.perf_counter() - t0, 1)
+        log(f"[bench] cpu oracle: {cpu_gbs:.3f} GB/s over {res['seconds']:.1f}s ({res['layers']} layers); "
+            f"other configs {cpu['stages']['configs_seconds']} s")
 
     out = {
         "metric": METRIC,

@@ -208,8 +208,9 @@ q4_status q4_from_canonical(const void* canon_codes, const void* canon_scales, c
                             void* packed, void* scales, void* zeros, void* stream);
 
 /* Measurement helper: read `bytes` (a positive multiple of 8192) from the device
- * buffer `buf` (16-byte aligned) with a plain streaming read kernel, one workgroup
- * per CU, so the GEMV's bytes / time can be compared with the read rate the same
+ * buffer `buf` (16-byte aligned) with a plain streaming read kernel (one workgroup of
+ * 4 wavefronts per CU, 8 KiB bursts per wavefront, pieces assigned round-robin: the
+ * fastest plain read measured), so the GEMV's bytes / time can be compared with the read rate the same
  * device sustains ([YBB] section 一: decode is bound by the bytes it reads). `sink`
  * is a device uint32 the kernel writes only in a case random data never produces.
  * Returns Q4_ERR_SHAPE for other sizes, Q4_ERR_NULL / Q4_ERR_ALIGN as usual. */

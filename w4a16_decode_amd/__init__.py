@@ -34,6 +34,8 @@ from .ops import (  # noqa: F401
     q8_workspace_bytes,
     quantize_pack,
     quantize_pack_clip,
+    quantize_pack_clip_into,
+    quantize_pack_into,
     quantize_pack_perm,
     read_probe,
     status_str,
@@ -44,7 +46,7 @@ from .ops import (  # noqa: F401
 )
 
 __all__ = [
-    "Q4Error", "QuantizedWeight", "quantize_pack", "quantize_pack_clip", "gemm", "gemm_noalloc", "gemm_config", "to_canonical",
+    "Q4Error", "QuantizedWeight", "quantize_pack", "quantize_pack_into", "quantize_pack_clip", "quantize_pack_clip_into", "gemm", "gemm_noalloc", "gemm_config", "to_canonical",
     "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "status_str", "version",
     "QuantizedWeight8", "q8_quantize_pack", "q8_gemm", "q8_gemm_config", "q8_to_canonical", "q8_from_canonical",
     "q8_packed_bytes", "q8_workspace_bytes",

@@ -113,12 +113,23 @@ def quantize_pack(W, group: int = 128, asym: bool = False) -> QuantizedWeight:
         raise ValueError("W must be 2-D [out_features, in_features]")
     out_features, in_features = W.shape
     qw = _alloc_qw(out_features, in_features, group, asym, W.device)
+    return quantize_pack_into(W, qw)
+
+
+def quantize_pack_into(W, qw: QuantizedWeight) -> QuantizedWeight:
+    """q4_quantize_pack / q4_quantize_pack_asym into the buffers of an existing
+    QuantizedWeight of the same shape, group and kind (allocates nothing)."""
+    import torch
+
+    _require_gpu(W, "W", torch.float16)
+    if tuple(W.shape) != (qw.out_features, qw.in_features):
+        raise ValueError("W does not match the QuantizedWeight's shape")
     lib = _lib.load()
-    if asym:
-        st = lib.q4_quantize_pack_asym(W.data_ptr(), out_features, in_features, group, qw.packed.data_ptr(),
+    if qw.asym:
+        st = lib.q4_quantize_pack_asym(W.data_ptr(), qw.out_features, qw.in_features, qw.group, qw.packed.data_ptr(),
                                        qw.scales.data_ptr(), qw.zeros.data_ptr(), _stream(W))
     else:
-        st = lib.q4_quantize_pack(W.data_ptr(), out_features, in_features, group, qw.packed.data_ptr(),
+        st = lib.q4_quantize_pack(W.data_ptr(), qw.out_features, qw.in_features, qw.group, qw.packed.data_ptr(),
                                   qw.scales.data_ptr(), _stream(W))
     _check(st)
     return qw
@@ -134,7 +145,17 @@ def quantize_pack_clip(W, group: int = 128, min_percent: int = 80) -> QuantizedW
         raise ValueError("W must be 2-D [out_features, in_features]")
     out_features, in_features = W.shape
     qw = _alloc_qw(out_features, in_features, group, False, W.device)
-    st = _lib.load().q4_quantize_pack_clip(W.data_ptr(), out_features, in_features, group, min_percent,
+    return quantize_pack_clip_into(W, qw, min_percent)
+
+
+def quantize_pack_clip_into(W, qw: QuantizedWeight, min_percent: int = 80) -> QuantizedWeight:
+    """q4_quantize_pack_clip into the buffers of an existing symmetric QuantizedWeight."""
+    import torch
+
+    _require_gpu(W, "W", torch.float16)
+    if tuple(W.shape) != (qw.out_features, qw.in_features) or qw.asym:
+        raise ValueError("W does not match the symmetric QuantizedWeight's shape")
+    st = _lib.load().q4_quantize_pack_clip(W.data_ptr(), qw.out_features, qw.in_features, qw.group, min_percent,
                                            qw.packed.data_ptr(), qw.scales.data_ptr(), _stream(W))
     _check(st)
     return qw

@@ -4,6 +4,12 @@
     python -m w4a16_decode_amd.profiling counters <counter_collection.csv> <name-filter>
     python -m w4a16_decode_amd.profiling traffic --fetch F.csv --write W.csv --cal-fetch CF.csv
                                                    --cal-write CW.csv --cal-bytes N --kernel FILTER
+    python -m w4a16_decode_amd.profiling split <kernel_trace.csv> <name-filter> <threshold_us> [label_below label_above]
+
+`split` divides the launches of the kernels matching the filter at a duration
+threshold (two matrices that share one kernel instance, e.g. the fused gate/up and
+q/k/v GEMVs) and prints each side's count and average duration; the line
+`<label_above>_avg_us_rocprof: X` is what bench.py reads back.
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per launch,
 each scaled by what the same counter reports for a plain device copy of a known
@@ -72,6 +78,16 @@ def traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_bytes: int, 
             "bytes": f_k * 1024 * f_scale + w_k * 1024 * w_scale}
 
 
+def split_durations(path: str, filt: str, threshold_us: float) -> tuple[list[float], list[float]]:
+    below, above = [], []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if filt in r["Kernel_Name"]:
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                (above if d >= threshold_us else below).append(d)
+    return below, above
+
+
 def main(argv):
     if not argv:
         print(__doc__)
@@ -90,6 +106,14 @@ def main(argv):
                     int(opts["--cal-bytes"]), opts["--kernel"])
         for k, v in t.items():
             print(f"{k}: {v:.6g}")
+        print(f"kernel_fingerprint: {kernel_fingerprint()}")
+    elif cmd == "split":
+        below, above = split_durations(argv[1], argv[2], float(argv[3]))
+        lb, la = (argv[4], argv[5]) if len(argv) > 5 else ("below", "above")
+        for label, v in ((lb, below), (la, above)):
+            if v:
+                print(f"{label}: {len(v)} launches, avg {statistics.mean(v):.2f} us, median {statistics.median(v):.2f} us")
+                print(f"{label}_avg_us_rocprof: {statistics.mean(v):.3f}")
         print(f"kernel_fingerprint: {kernel_fingerprint()}")
     elif cmd == "fingerprint":
         print(kernel_fingerprint())
