@@ -85,7 +85,8 @@ const char* q4_status_str(int status);
 /* Description of the last failure on the calling thread ("" if none). */
 const char* q4_last_error(void);
 
-/* Library version string, e.g. "q4 1.0.0 gfx950". */
+/* Library version string, "q4 1.0.0 gfx950 src <hash>": <hash> identifies the
+ * sources and flags the library was built from ("unknown" when built without them). */
 const char* q4_version(void);
 
 /* 1 if `group` is a supported group size, else 0. */

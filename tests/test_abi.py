@@ -53,6 +53,36 @@ def test_version_and_status_strings(lib):
     assert lib.q4_status_str(99) == b"unknown status"
 
 
+def test_library_built_from_this_tree(lib):
+    """The loaded library carries the hash of the sources and flags it was built from,
+    and it is this tree's: a library left over from other sources never runs."""
+    from w4a16_decode_amd.build import source_hash
+
+    h = source_hash()
+    assert lib.q4_version().decode().endswith(" src " + h)
+    assert source_hash(["-DQ4_EXTRA"]) != h
+
+
+def test_source_hash_does_not_depend_on_the_tree_location(tmp_path):
+    """The tree is built in one place and run from another (a copy elsewhere): the
+    hash covers file contents and flags, not absolute paths."""
+    import shutil
+    import subprocess
+    import sys
+
+    from w4a16_decode_amd.build import ROOT, source_hash
+
+    pkg = tmp_path / "w4a16_decode_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "w4a16_decode_amd", "build.py"), pkg / "build.py")
+    (pkg / "__init__.py").write_text("")
+    shutil.copytree(os.path.join(ROOT, "w4a16_decode_amd", "csrc"), pkg / "csrc")
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    out = subprocess.run([sys.executable, "-c", "from w4a16_decode_amd.build import source_hash; print(source_hash())"],
+                         cwd=tmp_path, capture_output=True, text=True, check=True).stdout.strip()
+    assert out == source_hash()
+
+
 def test_sizes(lib):
     assert lib.q4_packed_bytes(4096, 4096) == 4096 * 4096 // 2
     assert lib.q4_packed_bytes(17, 96) == 32 * 128 // 2          # padded to 16 rows, 128 channels

@@ -72,7 +72,8 @@ def header_functions(paths=HEADERS) -> list[str]:
 
 
 def load() -> ctypes.CDLL:
-    """Open libq4.so once. Raises if it has not been built."""
+    """Open libq4.so once. Raises if it has not been built, or was built from sources
+    other than the ones in this tree."""
     global _lib
     if _lib is not None:
         return _lib
@@ -86,5 +87,11 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    from .build import source_hash
+
+    built = lib.q4_version().decode().rsplit(" ", 1)[-1]
+    if built != source_hash():
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (library {built}, tree {source_hash()}): "
+                           "rebuild it with `python -m w4a16_decode_amd.build`")
     _lib = lib
     return lib

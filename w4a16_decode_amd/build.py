@@ -11,6 +11,7 @@ pointers from torch are valid in the library (one runtime per process).
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -35,6 +36,24 @@ COMMON = [
 ]
 
 
+def source_hash(extra_flags=()) -> str:
+    """Hash of everything the library is built from: the compile flags, the sources
+    and headers under csrc/ and the public headers under include/. The build bakes it
+    into q4_version(); the loader compares it with the tree it runs from, so a
+    library left over from other sources is never used."""
+    flags = " ".join(COMMON + list(extra_flags)).replace(ROOT, ".")  # the same wherever the tree is
+    h = hashlib.sha256(flags.encode())
+    inc = os.path.join(ROOT, "include")
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))] + \
+        [os.path.join(inc, f) for f in sorted(os.listdir(inc))]
+    for path in files:
+        if path.endswith((".cpp", ".hip", ".h")):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -52,7 +71,8 @@ def _run(cmd):
 def build(verbose: bool = False, extra_flags=None) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    flags = COMMON + list(extra_flags or [])
+    extra = list(extra_flags or [])
+    flags = COMMON + extra + [f'-DQ4_SOURCE_HASH="{source_hash(extra)}"']
     objs = []
     cmds = []
     for src in SOURCES:

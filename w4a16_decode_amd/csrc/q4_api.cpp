@@ -266,7 +266,10 @@ const char* q4_status_str(int status) {
 
 const char* q4_last_error(void) { return g_last_error; }
 
-const char* q4_version(void) { return "q4 1.0.0 gfx950"; }
+#ifndef Q4_SOURCE_HASH
+#define Q4_SOURCE_HASH "unknown"
+#endif
+const char* q4_version(void) { return "q4 1.0.0 gfx950 src " Q4_SOURCE_HASH; }
 
 int32_t q4_group_supported(int32_t group) { return group_ok(group) ? 1 : 0; }
 
