@@ -117,6 +117,29 @@ bool gemv_shape_ok(int B, int S, int KS, int W, int R, int group, bool asym, siz
   return (int64_t)B * nsb * 16 <= (int64_t)kGemvXChunks * W * 64;
 }
 
+// Modelled time (us) of a GEMV launch shape at 4 <= B <= 16 (symmetric INT4 codes,
+// one scale per block): a linear model of the busiest CU's work, fitted to launches of
+// every shape R in {1, 2}, W in {8, 16}, KS in {1, 2, 4, 8} on 16 weight matrices
+// (1024 to 57344 rows, 4096 to 28672 channels) at B = 4 to 16 on MI355X. Terms: KiB
+// of codes the busiest CU streams (0.0555 us each, 4.7 TB/s over 256 CUs); KiB of
+// activations it stages into LDS before streaming (0.0263 us each); the separate
+// split reduction (1.99 us, plus 0.92 us per MB of float32 partials); and a credit
+// for longer streams per wavefront (-0.297 us per KiB of codes per wavefront).
+// Picking the lowest-cost shape came within 1.4% on average (10.7% at worst) of the
+// fastest measured shape of each matrix and batch size.
+double gemv_model_us(int B, int T, int S, int N, int R, int W, int KS, size_t lds, size_t lds_limit, int cus) {
+  const int64_t nRB = (T + R - 1) / R;
+  const int64_t nsb = (S + KS - 1) / KS;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16 / W, (int64_t)(lds_limit / std::max<size_t>(lds, 1))));
+  const int64_t per_split = std::max<int64_t>(1, std::min<int64_t>(nRB, per_cu * cus / KS));
+  const int64_t n_rb = (nRB + per_split - 1) / per_split;
+  const int64_t wgs_cu = (per_split * KS + cus - 1) / cus;  // workgroups on the busiest CU
+  const double codes = (double)(n_rb * R * nsb * wgs_cu);  // KiB
+  const double xs = (double)B * nsb / 4.0 * wgs_cu;        // KiB
+  const double red = KS > 1 ? 1.99 + 0.92 * ((double)KS * B * N * 4 / 1e6) : 0.0;
+  return 0.0555 * codes + 0.0263 * xs + red - 0.297 * codes / (W * wgs_cu);
+}
+
 // LDS of one skinny-GEMM workgroup (q4_internal.h).
 size_t mfma_lds(int col_tiles) { return q4::mfma_lds_bytes(col_tiles); }
 
@@ -167,6 +190,23 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     a->waves_per_group = W;
     a->k_splits = KS;
     a->lds_limit = lim;
+    if (B >= 4 && !a->q8 && !a->asym && d.group >= 128) {
+      // the shape of lowest modelled time (gemv_model_us); ties keep fewer splits
+      const int cus = q4::device_cu_count_cached();
+      double best = 1e30;
+      for (int ks : {1, 2, 4, 8})
+        for (int r : {1, 2})
+          for (int w : {8, 16}) {
+            if (ks > S || !gemv_shape_ok(B, S, ks, w, r, d.group, false, lim)) continue;
+            const double t = gemv_model_us(B, T, S, d.Np, r, w, ks, gemv_lds(B, S, ks, r, d.group, false), lim, cus);
+            if (t < best) {
+              best = t;
+              a->rows_per_wave = r;
+              a->waves_per_group = w;
+              a->k_splits = ks;
+            }
+          }
+    }
     return;
   }
   // B > 16: skinny MFMA GEMM, 8 wavefronts per workgroup sharing CT column tiles of
