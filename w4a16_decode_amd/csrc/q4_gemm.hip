@@ -1097,14 +1097,9 @@ __global__ __launch_bounds__(WV * 64) void gemm_mfma_kernel(const uint16_t* __re
   }
 }
 
-// Blocks per chunk: the two activation buffers take about 132 KiB of LDS (one
-// workgroup per CU) whatever the column tiles.
-template <int CT>
-constexpr int mfma_chunk_blocks() { return 16 / CT; }
-
 template <int RT, int CT, int GSUB, bool ASYM, int WV, bool Q8 = false>
 hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t stream) {
-  constexpr int NB = mfma_chunk_blocks<CT>();
+  constexpr int NB = mfma_chunk_blocks(CT);
   const int T = a.Np / kTileRows;
   const int S = a.Kp / kSuperK;
   const int J = a.group >= kSuperK ? a.group / kSuperK : 1;
