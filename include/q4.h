@@ -217,6 +217,18 @@ q4_status q4_from_canonical(const void* canon_codes, const void* canon_scales, c
  * Returns Q4_ERR_SHAPE for other sizes, Q4_ERR_NULL / Q4_ERR_ALIGN as usual. */
 q4_status q4_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
 
+/* Self-check of the quantizers' code decision on this device ([YBB] section 二:
+ * q = round(w / scale), half to even). The quantizers take it from one hardware
+ * reciprocal per scale and a tie test instead of a divide per weight; this runs that
+ * decision on every positive finite float16 scale s and every finite float16 weight
+ * w (31,743 x 63,488 = 2,015,299,584 pairs) against rint of the correctly rounded
+ * float32 quotient, and counts the pairs with |w / s| < 341 (every clamp range used
+ * lies inside) where the two differ. `counts` is a device array of two uint64 that
+ * the call overwrites: counts[0] = pairs checked, counts[1] = mismatches (0 on a
+ * correct device). Enqueued on `stream` (a few milliseconds); Q4_ERR_NULL and
+ * Q4_ERR_ALIGN (8 bytes) as usual. */
+q4_status q4_rtn_check(uint64_t* counts, void* stream);
+
 /* ---- act-order (GPTQ desc_act) weights ----------------------------------------
  * [ARG] section 五.3: channels may be quantized in descending order of the Hessian
  * diagonal, groups of g being formed along that order, so a kernel needs a per-

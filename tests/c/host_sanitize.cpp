@@ -43,6 +43,10 @@ hipError_t launch_read_probe(const void*, int64_t, void*, int, hipStream_t) {
   ++g_launches;
   return g_launch_result;
 }
+hipError_t launch_rtn_check(unsigned long long*, hipStream_t) {
+  ++g_launches;
+  return g_launch_result;
+}
 int g_scratch_lookups = 0;
 hipError_t noalloc_scratch(void** out) {
   ++g_scratch_lookups;
@@ -180,6 +184,9 @@ int main() {
              Q4_ERR_SHAPE, 0);
   VALID(q4_read_probe(P, 8192 * 4, P, nullptr), 1);
   CHECK_CALL(q4_read_probe(P, 8191, P, nullptr), Q4_ERR_SHAPE, 0);
+  VALID(q4_rtn_check(reinterpret_cast<uint64_t*>(P), nullptr), 1);
+  CHECK_CALL(q4_rtn_check(nullptr, nullptr), Q4_ERR_NULL, 0);
+  CHECK_CALL(q4_rtn_check(reinterpret_cast<uint64_t*>(P + 4), nullptr), Q4_ERR_ALIGN, 0);
 
   // act-order permutation (host code): channel k in group (5k + 3) % 16, 4096 channels
   {

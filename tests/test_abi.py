@@ -300,3 +300,5 @@ def test_read_probe_validation(lib):
     assert lib.q4_read_probe(FAKE, 8000, FAKE, None) == 2
     assert lib.q4_read_probe(FAKE, 0, FAKE, None) == 2
     assert lib.q4_read_probe(FAKE + 8, 8192, FAKE, None) == 4
+    assert lib.q4_rtn_check(None, None) == 1
+    assert lib.q4_rtn_check(FAKE + 4, None) == 4

@@ -155,6 +155,17 @@ def test_kv_codes_every_fp16_value(q4, g):
     assert np.array_equal(to_np(cache.codes), oracle.pack_kv_int4(q_o).reshape(1, n, d // 2))
 
 
+def test_device_decision_every_fp16_pair(q4):
+    """q4_rtn_check: the kernels' division-free decision against rint of the correctly
+    rounded float32 quotient for every positive finite float16 scale and every finite
+    float16 weight, on the device itself (the host proof in test_rtn_decision models
+    v_rcp_f32 as within one ulp; this checks the hardware and the compiled code)."""
+    checked, bad = q4.rtn_check()
+    say(f"device decision: {checked} (w, s) pairs, {bad} mismatches")
+    assert checked == 31743 * 63488
+    assert bad == 0
+
+
 OFFSET_SHAPES = [(4096, 4096), (1024, 8192), (8192, 8192), (2048, 28672)]
 
 

@@ -38,6 +38,7 @@ from .ops import (  # noqa: F401
     quantize_pack_into,
     quantize_pack_perm,
     read_probe,
+    rtn_check,
     status_str,
     to_canonical,
     version,
@@ -51,5 +52,5 @@ __all__ = [
     "QuantizedWeight8", "q8_quantize_pack", "q8_gemm", "q8_gemm_config", "q8_to_canonical", "q8_from_canonical",
     "q8_packed_bytes", "q8_workspace_bytes",
     "ActOrderWeight", "actorder_perm", "quantize_pack_perm", "gemm_perm", "workspace_bytes_perm",
-    "KVCache4", "kv_cache_alloc", "kv_quantize_pack", "kv_dequant", "read_probe",
+    "KVCache4", "kv_cache_alloc", "kv_quantize_pack", "kv_dequant", "read_probe", "rtn_check",
 ]

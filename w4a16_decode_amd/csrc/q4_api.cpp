@@ -770,4 +770,12 @@ q4_status q4_read_probe(const void* buf, size_t bytes, void* sink, void* stream)
                                           static_cast<hipStream_t>(stream)), "read probe launch");
 }
 
+q4_status q4_rtn_check(uint64_t* counts, void* stream) {
+  if (!counts) return fail(Q4_ERR_NULL, "counts must be non-NULL");
+  if (!aligned(counts, 8)) return fail(Q4_ERR_ALIGN, "counts needs 8-byte alignment");
+  return hip_status(q4::launch_rtn_check(reinterpret_cast<unsigned long long*>(counts),
+                                         static_cast<hipStream_t>(stream)),
+                    "rtn check launch");
+}
+
 }  // extern "C"

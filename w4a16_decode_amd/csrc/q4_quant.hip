@@ -705,4 +705,50 @@ hipError_t launch_w8_from_canonical(const W8Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Self-check of the division-free decision (q4_rtn.h) on the device: for every
+// positive finite float16 scale s (one workgroup each) and every finite float16
+// weight w, rtn_quot(w, rtn_recip(s)) against rintf of the correctly rounded float32
+// quotient w / s (this file is built with correctly rounded division), counting the
+// pairs with |w / s| < 341 where the two differ. counts[0] += pairs checked,
+// counts[1] += mismatches (zeroed by the first kernel).
+namespace {
+
+constexpr int kPosFiniteFp16 = 0x7BFF;  // positive finite float16 bit patterns 0x0001..0x7BFF
+
+__global__ void rtn_check_zero_kernel(unsigned long long* counts) {
+  if (threadIdx.x < 2) counts[threadIdx.x] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void rtn_check_kernel(unsigned long long* counts) {
+  const uint16_t sb = (uint16_t)(blockIdx.x + 1);
+  const float s = (float)__builtin_bit_cast(_Float16, sb);
+  const float r = rtn_recip(s);
+  unsigned int bad = 0, checked = 0;
+  for (int i = threadIdx.x; i < 2 * (kPosFiniteFp16 + 1); i += blockDim.x) {
+    const uint16_t wb = (uint16_t)(i <= kPosFiniteFp16 ? i : 0x8000 + (i - kPosFiniteFp16 - 1));
+    const float w = (float)__builtin_bit_cast(_Float16, wb);
+    const float q = w / s;
+    ++checked;
+    if (fabsf(q) < 341.0f && rtn_quot(w, r) != rintf(q)) ++bad;
+  }
+  // wavefront sums, then one atomic per wavefront
+  for (int m = 32; m >= 1; m >>= 1) {
+    bad += __shfl_xor(bad, m);
+    checked += __shfl_xor(checked, m);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&counts[0], (unsigned long long)checked);
+    atomicAdd(&counts[1], (unsigned long long)bad);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rtn_check(unsigned long long* counts, hipStream_t stream) {
+  hipLaunchKernelGGL(rtn_check_zero_kernel, dim3(1), dim3(64), 0, stream, counts);
+  hipLaunchKernelGGL(rtn_check_kernel, dim3(kPosFiniteFp16), dim3(256), 0, stream, counts);
+  return hipGetLastError();
+}
+
 }  // namespace q4

@@ -315,6 +315,17 @@ def read_probe(buf, sink) -> None:
     _check(_lib.load().q4_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)))
 
 
+def rtn_check(device=None) -> tuple[int, int]:
+    """q4_rtn_check: (pairs checked, mismatches) of the quantizers' division-free code
+    decision against the correctly rounded quotient, every float16 scale and weight."""
+    import torch
+
+    counts = torch.zeros(2, dtype=torch.int64, device=device or "cuda")
+    _check(_lib.load().q4_rtn_check(counts.data_ptr(), _stream(counts)))
+    c = counts.cpu().tolist()
+    return int(c[0]), int(c[1])
+
+
 def workspace_bytes_perm(batch: int, out_features: int, in_features: int, group: int) -> int:
     return int(_lib.load().q4_workspace_bytes_perm(batch, out_features, in_features, group))
 
