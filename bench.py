@@ -263,6 +263,7 @@ def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
         flops = perfmodel.gemm_flops(B, N, K)
         nbytes = perfmodel.gemm_read_bytes(B, N, K, group)
         out[str(B)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                       "pct_of_hbm_peak": round(nbytes / t / 1e9 / perfmodel.HBM_PEAK_GBS, 4),
                        "TFLOPs": round(flops / t / 1e12, 2),
                        "mfma_util": round(flops / t / 1e12 / perfmodel.MFMA_FP16_DENSE_TFLOPS, 4),
                        "bf16_dense_us": round(td * 1e6, 2), "speedup_vs_bf16": round(td / t, 3)}
@@ -704,6 +705,18 @@ def main(argv=None):
 
     extras = {}
     if not args.no_extras:
+        # every matrix kind of the layer at B = 1, timed like the roofline kernel (its 80
+        # launches back to back in a HIP graph), each against the 8 TB/s peak and the read probe
+        per_matrix = {}
+        for name, kind in KIND_OF.items():
+            d, qwk, _ = sweep.time_kernel(name)
+            nb = perfmodel.gemm_read_bytes(1, qwk.out_features, qwk.in_features, group)
+            per_matrix[kind] = {"shape": [qwk.out_features, qwk.in_features], "us": round(d * 1e6, 2),
+                                "GBps": round(nb / d / 1e9, 1),
+                                "pct_of_hbm_peak": round(nb / d / 1e9 / perfmodel.HBM_PEAK_GBS, 4),
+                                "frac_of_measured_read": round(nb / d / 1e9 / read_gbs, 4)}
+        extras["per_matrix_b1_70b"] = per_matrix
+        log(f"[bench] per matrix at B=1: {per_matrix}")
         per_layer = {}
         for B in (1, 2, 4, 8):
             sw = sweep if B == 1 else Sweep(model, B, seed=3, device=dev)
