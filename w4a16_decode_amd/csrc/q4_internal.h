@@ -105,8 +105,8 @@ constexpr int kGemmRowPad = 16;
 // Skinny GEMM: the channel range is walked in chunks of 8 / col_tiles blocks, at least
 // 2 (the ring of codes in flight is one chunk long). LDS: two activation tiles of
 // col_tiles * 16 batch rows by one chunk, padded rows -- ~66-68 KiB for 2 or 4 column
-// tiles (two workgroups per CU), ~136 KiB for 8. Chunks of 16 / col_tiles blocks (one
-// workgroup per CU at every width) measured 5-12% slower at B = 24-32.
+// tiles (room for two workgroups per CU), ~136 KiB for 8. Chunks of 16 / col_tiles
+// blocks (~132 KiB at every width) measured 5-12% slower at B = 24-32.
 constexpr int mfma_chunk_blocks(int col_tiles) { return col_tiles >= 4 ? 2 : 8 / col_tiles; }
 constexpr size_t mfma_lds_bytes(int col_tiles) {
   return (size_t)2 * col_tiles * 16 * (mfma_chunk_blocks(col_tiles) * 128 + kGemmRowPad) * 2;
