@@ -126,7 +126,8 @@ int main() {
 
   // products: every path of the shape selection, with enough workspace
   static const int64_t shapes[][3] = {{1, 57344, 8192}, {1, 8192, 28672}, {4, 8192, 28672}, {8, 10240, 8192},
-                                      {16, 4096, 4096}, {32, 28672, 8192}, {256, 28672, 8192}, {3, 17, 96}};
+                                      {16, 4096, 4096}, {32, 28672, 8192}, {256, 28672, 8192}, {3, 17, 96},
+                                      {48, 4096, 14336}, {192, 8192, 8192}, {256, 6144, 4096}};
   for (const auto& sh : shapes) {
     const int64_t B = sh[0], N = sh[1], K = sh[2];
     const int32_t g = K % 128 == 0 ? 128 : 32;
