@@ -366,6 +366,17 @@ def test_full_batch_sweep_28672x8192(q4):
     _full_size_check(q4, 28672, 8192, 128, (1, 4, 16, 32, 64, 128, 256), seed=4, nrows=64)
 
 
+@pytest.mark.parametrize("N,K,Bs", [(8192, 28672, (5, 12, 17, 48)), (8192, 8192, (16, 192)),
+                                    (6144, 4096, (256,)), (4096, 14336, (6, 32, 64))])
+def test_full_launch_rules(q4, N, K, Bs):
+    """Full-size matrices at the batch sizes where the launch-shape rules take their less
+    common branches: the GEMV cost model's 8-way channel splits (down at B = 5, 12),
+    rows of >= 112 blocks split 8 ways in the skinny GEMM (B = 17-64), and short rows at
+    B > 128 on 2 column tiles without a split (8192x8192 at 192, 6144x4096 at 256)."""
+    say(f"launch rules {N}x{K} B={Bs}")
+    _full_size_check(q4, N, K, 128, Bs, seed=N % 97, nrows=64)
+
+
 def test_full_fused_gate_up_batches(q4):
     """The fused 70B gate/up matrix (57344x8192, device-generated weights) at B = 16,
     64, 128 and 256: B = 128 takes the wider column groups that keep its skinny-GEMM
