@@ -78,9 +78,18 @@ def test_source_hash_does_not_depend_on_the_tree_location(tmp_path):
     (pkg / "__init__.py").write_text("")
     shutil.copytree(os.path.join(ROOT, "w4a16_decode_amd", "csrc"), pkg / "csrc")
     shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
-    out = subprocess.run([sys.executable, "-c", "from w4a16_decode_amd.build import source_hash; print(source_hash())"],
-                         cwd=tmp_path, capture_output=True, text=True, check=True).stdout.strip()
-    assert out == source_hash()
+    def copy_hash():
+        return subprocess.run([sys.executable, "-c", "from w4a16_decode_amd.build import source_hash; print(source_hash())"],
+                              cwd=tmp_path, capture_output=True, text=True, check=True).stdout.strip()
+
+    assert copy_hash() == source_hash()
+    # comments and layout are not code: editing them keeps the hash, editing code does not
+    hdr = tmp_path / "include" / "q4.h"
+    text = hdr.read_text()
+    hdr.write_text("/* a note */\n" + text.replace("\n", "\n\n", 5))
+    assert copy_hash() == source_hash()
+    hdr.write_text(text.replace("q4_version", "q4_version2", 1))
+    assert copy_hash() != source_hash()
 
 
 def test_sizes(lib):

@@ -36,11 +36,37 @@ COMMON = [
 ]
 
 
+def code_only(src: str) -> str:
+    """C++ source without comments and with all whitespace runs collapsed (string and
+    character literals kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(extra_flags=()) -> str:
-    """Hash of everything the library is built from: the compile flags, the sources
-    and headers under csrc/ and the public headers under include/. The build bakes it
-    into q4_version(); the loader compares it with the tree it runs from, so a
-    library left over from other sources is never used."""
+    """Hash of everything the library is built from: the compile flags, the code of
+    the sources and headers under csrc/ and of the public headers under include/
+    (comments and layout ignored). The build bakes it into q4_version(); the loader
+    compares it with the tree it runs from, so a library left over from other
+    sources is never used."""
     flags = " ".join(COMMON + list(extra_flags)).replace(ROOT, ".")  # the same wherever the tree is
     h = hashlib.sha256(flags.encode())
     inc = os.path.join(ROOT, "include")
@@ -49,8 +75,8 @@ def source_hash(extra_flags=()) -> str:
     for path in files:
         if path.endswith((".cpp", ".hip", ".h")):
             h.update(os.path.basename(path).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

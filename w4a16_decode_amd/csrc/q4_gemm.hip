@@ -56,10 +56,9 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 // streaming alone at the end). Each wavefront streams the blocks of codes and
 // scales of its units through a ring of P stages (vector loads retire in order, so
 // only weights ride that pipeline): INT4 codes with one row tile per wavefront fill
-// the ring in bursts of P/2 consecutive blocks, one half loading while the other
-// is computed (back-to-back loads of neighbouring kilobytes stream faster than
-// the same loads spread out), the other kinds keep a rolling window of P-1 blocks
-// in flight. Activation operands are read from LDS: the
+// the ring in bursts of P/2 blocks of the unit, one half loading while the other
+// is computed (back-to-back loads stream faster than the same loads spread out),
+// the other kinds keep a rolling window of P-1 blocks in flight. Activation operands are read from LDS: the
 // workgroup copies its slice of x (all B rows) into LDS once. The units a
 // wavefront starts with are fixed (wave, wave + W, ...: as many as its first loads
 // can reach, normally one) and only later ones come from the counter, so every

@@ -15,8 +15,9 @@ q/k/v GEMVs) and prints each side's count and average duration; the line
 each scaled by what the same counter reports for a plain device copy of a known
 size (the copy reads and writes cal-bytes each).
 
-The kernel fingerprint (kernel_fingerprint) hashes the GEMV sources; a traffic
-figure recorded under profiles/ is only valid while it matches.
+The kernel fingerprint (kernel_fingerprint) hashes the GEMV sources with comments and
+whitespace removed (the code the compiler sees); a figure recorded under profiles/ is
+only used while it matches.
 """
 
 from __future__ import annotations
@@ -28,15 +29,18 @@ import statistics
 import sys
 from collections import defaultdict
 
+from .build import code_only
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/q4_gemm.hip", "csrc/q4_device.h")
 
 
-def kernel_fingerprint() -> str:
+def kernel_fingerprint(sources=None) -> str:
+    """Hash of the GEMV kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
+    for path in sources or [os.path.join(HERE, rel) for rel in KERNEL_SOURCES]:
+        with open(path, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
