@@ -737,9 +737,16 @@ def main(argv=None):
         s8 = Sweep(m8, 1, seed=2, device=dev)
         s8.capture()
         t8 = s8.time_steps(args.steps, args.warmup)
+        per_matrix8 = {}
+        for name, kind in KIND_OF.items():
+            d, qwk, _ = s8.time_kernel(name)
+            nb = perfmodel.gemm_read_bytes(1, qwk.out_features, qwk.in_features, group)
+            per_matrix8[kind] = {"shape": [qwk.out_features, qwk.in_features], "us": round(d * 1e6, 2),
+                                 "GBps": round(nb / d / 1e9, 1),
+                                 "pct_of_hbm_peak": round(nb / d / 1e9 / perfmodel.HBM_PEAK_GBS, 4)}
         extras["sweep_8b_b1"] = {"ms_per_step": round(t8 * 1e3, 4), "GBps": round(s8.bytes_per_step() / t8 / 1e9, 1),
                                  "pct_of_hbm_peak": round(s8.bytes_per_step() / t8 / 1e9 / perfmodel.HBM_PEAK_GBS, 4),
-                                 "us_per_layer": round(t8 / 32 * 1e6, 2)}
+                                 "us_per_layer": round(t8 / 32 * 1e6, 2), "per_matrix": per_matrix8}
         log(f"[bench] 8B sweep: {extras['sweep_8b_b1']}")
         del s8, m8
 
