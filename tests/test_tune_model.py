@@ -65,6 +65,10 @@ def test_features_hand_case():
 def test_library_splits_follow_the_model(N, K, B):
     """Without a GPU the library sizes for 64 KiB of LDS per workgroup and 256 CUs; its
     channel splits (the workspace it asks for) must be the model's pick for those."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a visible GPU sets the library's limits; the GPU tests run its launches")
     lib = _lib.load()
     code = _code_coefficients() + [0.0]
     p = tune_gemv.pick(N, K, B, code, lds_limit=64 * 1024, cus=256)
