@@ -223,8 +223,12 @@ def recorded_traffic():
     return recorded_value(TRAFFIC_PROFILE, "bytes")
 
 
+SWEEP_B = (1, 4, 16, 32, 48, 64, 96, 128, 192, 256)  # batch sizes of the 28672x8192 sweep
+
+
 def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
-    """28672x8192: W4A16 at B in {1,4,16,32,64,128,256} vs dense bf16 torch.mm."""
+    """28672x8192: W4A16 at B in {1,4,16,32,48,64,96,128,192,256} vs dense bf16 torch.mm,
+    with the launch shape the library picks at each B."""
     import torch
 
     import synth
@@ -242,7 +246,7 @@ def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
     for c in range(3):  # 3 x 470 MB bf16, stored [K, N] so torch.mm needs no transpose
         dense.append(synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev).to(torch.bfloat16).t().contiguous())
     out = {}
-    for B in (1, 4, 16, 32, 64, 128, 256):
+    for B in SWEEP_B:
         x = synth.device_activation(B, K, seed=4, layer=0, matrix=0, device=dev)
         y = torch.empty((B, N), dtype=torch.float16, device=dev)
         ws = torch.empty(max(16, q4.workspace_bytes(B, N, K, group)), dtype=torch.uint8, device=dev)
@@ -266,7 +270,8 @@ def extras_batch_sweep(dev, group: int, log_prefix="[bench]"):
                        "pct_of_hbm_peak": round(nbytes / t / 1e9 / perfmodel.HBM_PEAK_GBS, 4),
                        "TFLOPs": round(flops / t / 1e12, 2),
                        "mfma_util": round(flops / t / 1e12 / perfmodel.MFMA_FP16_DENSE_TFLOPS, 4),
-                       "bf16_dense_us": round(td * 1e6, 2), "speedup_vs_bf16": round(td / t, 3)}
+                       "bf16_dense_us": round(td * 1e6, 2), "speedup_vs_bf16": round(td / t, 3),
+                       "launch_shape_R_W_KS_CT": list(q4.gemm_shape(B, N, K, group))}
         log(f"{log_prefix} 28672x8192 B={B}: {t * 1e6:.1f} us ({nbytes / t / 1e9:.0f} GB/s, "
             f"{flops / t / 1e12:.1f} TFLOP/s) vs bf16 mm {td * 1e6:.1f} us")
     crossover = next((int(b) for b, v in out.items() if v["speedup_vs_bf16"] < 1.0), None)
@@ -545,7 +550,7 @@ def cpu_configs(dev, group: int) -> dict:
     wh, td = timed(lambda: oracle.dequant_sym(q, s, group))
     del q, s
     per_b = {}
-    for B in (1, 4, 16, 32, 64, 128, 256):
+    for B in SWEEP_B:
         x = synth.activation(B, K, seed=4)
         y, tm = timed(lambda: oracle.gemm_ref(x, wh))
         assert np.all(np.isfinite(y))

@@ -140,6 +140,15 @@ q4_status q4_quantize_pack_clip(const void* W, int64_t out, int64_t in, int32_t 
  * workspace is scratch: its contents on entry are ignored and undefined on return. */
 size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group);
 
+/* The launch shape q4_gemm picks for this product on the current device, as the
+ * arguments q4_gemm_config takes to run the same launch: shape[0] = rows_per_wave,
+ * shape[1] = waves_per_group, shape[2] = k_splits, shape[3] = col_tiles (4 int32
+ * written on success). A host-side query that touches no device memory; it holds for
+ * symmetric codes (q4_gemm_asym may pick another shape). Returns Q4_ERR_NULL for a
+ * NULL shape, Q4_ERR_SHAPE for B outside [1, 2^30) and the errors of q4_gemm for
+ * out, in and group. */
+q4_status q4_gemm_shape(int64_t B, int64_t out, int64_t in, int32_t group, int32_t* shape);
+
 /* Fused W4A16 product ([ARG] sections 二.2 and 二.3; [YBB] section 一):
  *   y[b][n] = float16_rne( sum_j s16[n][j] * sum_{k in group j} x[b][k] * q[n][k] )
  * with float16 x and codes, float32 accumulation, the group scale applied to
@@ -185,10 +194,10 @@ q4_status q4_gemm_asym(const void* x, int64_t B, const void* packed, const void*
  *   k_splits * B * out * 4 bytes of workspace when k_splits > 1.
  * B > 16 (skinny GEMM): `rows_per_wave` 1, 2 or 4, `waves_per_group` 4 or 8
  *   (8 only with rows_per_wave <= 2),
- *   `col_tiles` 2, 4 or 8 tiles of 16 batch rows per workgroup, with
+ *   `col_tiles` 2, 3, 4, 6 or 8 tiles of 16 batch rows per workgroup, with
  *   rows_per_wave * col_tiles * max(1, 128 / group) <= 16 (accumulator
  *   registers), `k_splits` workgroups splitting the channel range in chunks of
- *   16 / col_tiles blocks of 128 (at most as many splits as chunks). Needs
+ *   max(2, 8 / col_tiles) blocks of 128 (at most as many splits as chunks). Needs
  *   k_splits * B * out * 4 bytes of workspace when k_splits > 1. */
 q4_status q4_gemm_config(const void* x, int64_t B, const void* packed, const void* scales,
                          const void* zeros, int32_t asym, int64_t out, int64_t in, int32_t group,

@@ -47,6 +47,10 @@ hipError_t launch_rtn_check(unsigned long long*, hipStream_t) {
   ++g_launches;
   return g_launch_result;
 }
+// the MI355X residency of the skinny GEMM's symmetric kernels: one row tile per
+// wavefront with at most 4 column tiles (90-104 VGPRs, <= 68 KiB of LDS) fits two
+// 8-wavefront workgroups per CU, every other shape one
+int mfma_resident_per_cu(int rows_per_wave, int col_tiles) { return rows_per_wave == 1 && col_tiles <= 4 ? 2 : 1; }
 int g_scratch_lookups = 0;
 hipError_t noalloc_scratch(void** out) {
   ++g_scratch_lookups;
@@ -107,7 +111,23 @@ static char* const P = reinterpret_cast<char*>(0x100000);  // aligned, never der
     g_launch_result = hipSuccess;                                                        \
   } while (0)
 
-int main() {
+// `host_sanitize shapes`: reads "B out in group" lines from stdin and prints the
+// launch shape q4_gemm_shape reports for each ("R W KS CT", or "error <status>"),
+// with the device limits the stubs above stand in for (256 CUs, 160 KiB of LDS).
+static int print_shapes() {
+  long long B, N, K;
+  int g;
+  while (scanf("%lld %lld %lld %d", &B, &N, &K, &g) == 4) {
+    int32_t sh[4] = {0, 0, 0, 0};
+    const q4_status st = q4_gemm_shape(B, N, K, g, sh);
+    if (st != Q4_OK) printf("error %d\n", (int)st);
+    else printf("%d %d %d %d\n", (int)sh[0], (int)sh[1], (int)sh[2], (int)sh[3]);
+  }
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && strcmp(argv[1], "shapes") == 0) return print_shapes();
   // quantize
   VALID(q4_quantize_pack(P, 4096, 4096, 128, P, P, nullptr), 1);
   VALID(q4_quantize_pack_asym(P, 300, 1024, 64, P, P, P, nullptr), 1);
@@ -140,6 +160,19 @@ int main() {
     if (ws > 0) CHECK_CALL(q4_gemm(P, B, P, P, N, K, g, P, P, ws - 1, nullptr), Q4_ERR_WORKSPACE, 0);
     const size_t w8 = q8_workspace_bytes(B, N, K);
     VALID(q8_gemm(P, B, P, P, N, K, P, P, w8, nullptr), 1);
+  }
+  // launch-shape query: host only, argument errors as q4_gemm's
+  {
+    int32_t sh[4] = {0, 0, 0, 0};
+    CHECK_CALL(q4_gemm_shape(1, 57344, 8192, 128, sh), Q4_OK, 0);
+    EXPECT(sh[3] == 1 && sh[0] >= 1 && sh[1] >= 1 && sh[2] >= 1, "B <= 16 runs the GEMV (one column tile)");
+    CHECK_CALL(q4_gemm_shape(96, 28672, 8192, 128, sh), Q4_OK, 0);
+    EXPECT(sh[1] == 8 && (sh[3] == 3 || sh[3] == 6), "B = 96: six 16-row tiles, in groups of 3 or 6");
+    CHECK_CALL(q4_gemm_shape(96, 28672, 8192, 128, nullptr), Q4_ERR_NULL, 0);
+    CHECK_CALL(q4_gemm_shape(0, 28672, 8192, 128, sh), Q4_ERR_SHAPE, 0);
+    CHECK_CALL(q4_gemm_shape(int64_t(1) << 30, 28672, 8192, 128, sh), Q4_ERR_SHAPE, 0);
+    CHECK_CALL(q4_gemm_shape(4, 28672, 8192, 48, sh), Q4_ERR_GROUP, 0);
+    CHECK_CALL(q4_gemm_shape(4, 0, 8192, 128, sh), Q4_ERR_SHAPE, 0);
   }
   // the no-allocation product: the library scratch stands in for the workspace
   q4::g_scratch_lookups = 0;

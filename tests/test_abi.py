@@ -148,7 +148,7 @@ def test_gemm_validation(lib):
     assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 8, 2, 4, None, 0, None) == 5   # k_splits, B > 16
     assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 4, 4, 1, 8, None, 0, None) == 5   # R*CT > 16
     assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 32, FAKE, 2, 4, 1, 4, None, 0, None) == 5    # R*CT*4 > 16
-    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 4, 1, 3, None, 0, None) == 5   # col_tiles
+    assert c(FAKE, 64, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 4, 1, 5, None, 0, None) == 5   # col_tiles
     assert c(FAKE, 4, FAKE, FAKE, None, 0, 16, 128, 128, FAKE, 1, 1, 1, 2, None, 0, None) == 5    # GEMV: 1 tile
     # split k needs workspace: 2 * 1 * 16 * 4 bytes here
     assert c(FAKE, 1, FAKE, FAKE, None, 0, 16, 256, 128, FAKE, 1, 1, 2, 1, None, 0, None) == 6

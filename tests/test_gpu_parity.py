@@ -264,7 +264,7 @@ def test_gemm_mfma_shapes_agree(q4, B, g, asym):
     gsub = max(1, 128 // g)
     ran = 0
     for R in (1, 2, 4):
-        for CT in (2, 4, 8):
+        for CT in (2, 3, 4, 6, 8):
             say(f"  config B={B} g={g} R={R} CT={CT}")
             try:
                 y1 = to_np(q4.gemm_config(xg, qw, R, 4, 1, col_tiles=CT))
@@ -363,17 +363,19 @@ def test_full_8b_shapes(q4, name):
 
 def test_full_batch_sweep_28672x8192(q4):
     say("28672x8192 batch sweep")
-    _full_size_check(q4, 28672, 8192, 128, (1, 4, 16, 32, 64, 128, 256), seed=4, nrows=64)
+    _full_size_check(q4, 28672, 8192, 128, (1, 4, 16, 32, 48, 64, 96, 128, 192, 256), seed=4, nrows=64)
 
 
-@pytest.mark.parametrize("N,K,Bs", [(8192, 28672, (5, 12, 17, 48)), (8192, 8192, (16, 192)),
-                                    (6144, 4096, (256,)), (4096, 14336, (6, 32, 64))])
+@pytest.mark.parametrize("N,K,Bs", [(8192, 28672, (5, 12, 17, 48, 80, 192)), (8192, 8192, (16, 192)),
+                                    (6144, 4096, (144, 256)), (4096, 14336, (6, 32, 64)),
+                                    (28672, 8192, (40, 96, 144))])
 def test_full_launch_rules(q4, N, K, Bs):
-    """Full-size matrices at the batch sizes where the launch-shape rules take their less
-    common branches: the GEMV cost model's 8-way channel splits (down at B = 5, 12),
-    rows of >= 112 blocks split 8 ways in the skinny GEMM (B = 17-64), and short rows at
-    B > 128 on 2 column tiles without a split (8192x8192 at 192, 6144x4096 at 256)."""
-    say(f"launch rules {N}x{K} B={Bs}")
+    """Full-size matrices at the batch sizes where the launch-shape choices take their
+    less common branches: the GEMV cost model's 8-way channel splits (down at B = 5, 12),
+    and the skinny-GEMM model's 8-way splits of long rows (B = 17-192), groups of 3 and
+    6 column tiles (B = 40-192) and short rows on 2 column tiles in several groups
+    (6144x4096 at 144 and 256)."""
+    say(f"launch rules {N}x{K} B={Bs} shapes {[q4.gemm_shape(B, N, K, 128) for B in Bs]}")
     _full_size_check(q4, N, K, 128, Bs, seed=N % 97, nrows=64)
 
 

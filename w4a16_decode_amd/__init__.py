@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     gemm_config,
     gemm_noalloc,
     gemm_perm,
+    gemm_shape,
     groups_count,
     kv_cache_alloc,
     kv_dequant,
@@ -48,7 +49,7 @@ from .ops import (  # noqa: F401
 
 __all__ = [
     "Q4Error", "QuantizedWeight", "quantize_pack", "quantize_pack_into", "quantize_pack_clip", "quantize_pack_clip_into", "gemm", "gemm_noalloc", "gemm_config", "to_canonical",
-    "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "status_str", "version",
+    "from_canonical", "packed_bytes", "groups_count", "workspace_bytes", "gemm_shape", "status_str", "version",
     "QuantizedWeight8", "q8_quantize_pack", "q8_gemm", "q8_gemm_config", "q8_to_canonical", "q8_from_canonical",
     "q8_packed_bytes", "q8_workspace_bytes",
     "ActOrderWeight", "actorder_perm", "quantize_pack_perm", "gemm_perm", "workspace_bytes_perm",

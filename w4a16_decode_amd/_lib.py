@@ -31,6 +31,7 @@ SIGNATURES = {
     "q4_packed_bytes": (_SZ, [_I64, _I64]),
     "q4_groups_count": (_SZ, [_I64, _I64, _I32]),
     "q4_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "q4_gemm_shape": (ctypes.c_int, [_I64, _I64, _I64, _I32, _P]),
     "q4_quantize_pack": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "q4_quantize_pack_asym": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "q4_quantize_pack_clip": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P]),

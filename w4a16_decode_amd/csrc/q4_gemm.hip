@@ -1135,6 +1135,18 @@ hipError_t launch_mfma_a(const GemmArgs& a, hipStream_t stream) {
   return a.asym ? launch_mfma_g<RT, CT, true>(a, stream) : launch_mfma_g<RT, CT, false>(a, stream);
 }
 
+template <int RT, int CT>
+int mfma_resident_t() {
+  const void* fn =
+      reinterpret_cast<const void*>(&gemm_mfma_kernel<RT, CT, 1, false, mfma_chunk_blocks(CT), 8, false>);
+  return resident_per_cu(fn, 8 * kWave, mfma_lds_bytes(CT));
+}
+
+template <int CT>
+int mfma_resident_r(int rows_per_wave) {
+  return rows_per_wave == 1 ? mfma_resident_t<1, CT>() : mfma_resident_t<2, CT>();
+}
+
 template <int CT>
 hipError_t launch_mfma_r(const GemmArgs& a, hipStream_t stream) {
   if (a.rows_per_wave == 1) return launch_mfma_a<1, CT>(a, stream);
@@ -1196,6 +1208,16 @@ hipError_t noalloc_scratch(void** out) {
   return hipSuccess;
 }
 
+int mfma_resident_per_cu(int rows_per_wave, int col_tiles) {
+  switch (col_tiles) {
+    case 2: return mfma_resident_r<2>(rows_per_wave);
+    case 3: return mfma_resident_r<3>(rows_per_wave);
+    case 4: return mfma_resident_r<4>(rows_per_wave);
+    case 6: return mfma_resident_r<6>(rows_per_wave);
+    default: return mfma_resident_r<8>(rows_per_wave);
+  }
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.perm) {
     // gather x into the front of the workspace, then the plain GEMV / skinny GEMM
@@ -1215,7 +1237,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.B <= 16) return launch_gemv(a, stream);
   switch (a.col_tiles) {
     case 2: return launch_mfma_r<2>(a, stream);
+    case 3: return launch_mfma_r<3>(a, stream);
     case 4: return launch_mfma_r<4>(a, stream);
+    case 6: return launch_mfma_r<6>(a, stream);
     default: return launch_mfma_r<8>(a, stream);
   }
 }

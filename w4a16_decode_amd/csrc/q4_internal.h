@@ -104,9 +104,10 @@ constexpr int kGemmRowPad = 16;
 
 // Skinny GEMM: the channel range is walked in chunks of 8 / col_tiles blocks, at least
 // 2 (the ring of codes in flight is one chunk long). LDS: two activation tiles of
-// col_tiles * 16 batch rows by one chunk, padded rows -- ~66-68 KiB for 2 or 4 column
-// tiles (room for two workgroups per CU), ~136 KiB for 8. Chunks of 16 / col_tiles
-// blocks (~132 KiB at every width) measured 5-12% slower at B = 24-32.
+// col_tiles * 16 batch rows by one chunk, padded rows -- ~51 KiB for 3 column tiles,
+// ~66-68 KiB for 2 or 4 (room for two workgroups per CU), ~102 KiB for 6 and ~136 KiB
+// for 8. Chunks of 16 / col_tiles blocks (~132 KiB at every width) measured 5-12%
+// slower at B = 24-32.
 constexpr int mfma_chunk_blocks(int col_tiles) { return col_tiles >= 4 ? 2 : 8 / col_tiles; }
 constexpr size_t mfma_lds_bytes(int col_tiles) {
   return (size_t)2 * col_tiles * 16 * (mfma_chunk_blocks(col_tiles) * 128 + kGemmRowPad) * 2;
@@ -125,5 +126,10 @@ inline bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
 int device_cu_count_cached();
 int resident_per_cu(const void* fn, int block, size_t lds);
 int resident_grid(const void* fn, int block);
+
+// Workgroups of the skinny GEMM for symmetric INT4 codes with one scale per block
+// (8 wavefronts, rows_per_wave 1 or 2, col_tiles 2, 3, 4, 6 or 8) that one CU of the
+// current device holds at once (q4_gemm.hip); 1 where the device cannot be queried.
+int mfma_resident_per_cu(int rows_per_wave, int col_tiles);
 
 }  // namespace q4

@@ -7,6 +7,7 @@ stream to libq4. They do no arithmetic of their own.
 
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 
 from . import _lib
@@ -45,6 +46,14 @@ def groups_count(out_features: int, in_features: int, group: int) -> int:
 
 def workspace_bytes(batch: int, out_features: int, in_features: int, group: int) -> int:
     return int(_lib.load().q4_workspace_bytes(batch, out_features, in_features, group))
+
+
+def gemm_shape(batch: int, out_features: int, in_features: int, group: int) -> tuple:
+    """q4_gemm_shape (host): the launch shape q4_gemm picks on the current device, as
+    (rows_per_wave, waves_per_group, k_splits, col_tiles) -- gemm_config's arguments."""
+    shape = (ctypes.c_int32 * 4)()
+    _check(_lib.load().q4_gemm_shape(batch, out_features, in_features, group, shape))
+    return tuple(int(v) for v in shape)
 
 
 def _stream(t) -> int:
