@@ -259,10 +259,12 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     double best = 1e30;
     for (int ct : {2, 3, 4, 6, 8}) {
       if (ct > 2 && ct > col_tiles_total + 1) continue;
-      for (int r : {1, 2})
+      for (int r : {1, 2}) {
+        if (!mfma_shape_ok(r, 8, 1, ct, d.group, S)) continue;
+        const int per_cu = q4::mfma_resident_per_cu(r, ct);
         for (int ks : {1, 2, 3, 4, 6, 8}) {
           if (!mfma_shape_ok(r, 8, ks, ct, d.group, S)) continue;
-          const double t = skinny_model_us(B, T, S, d.N, r, ks, ct, q4::mfma_resident_per_cu(r, ct), cus);
+          const double t = skinny_model_us(B, T, S, d.N, r, ks, ct, per_cu, cus);
           if (t < best) {
             best = t;
             a->rows_per_wave = r;
@@ -271,6 +273,7 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
             a->col_tiles = ct;
           }
         }
+      }
     }
     if (best < 1e30) return;
   }
