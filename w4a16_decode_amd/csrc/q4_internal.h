@@ -47,9 +47,9 @@ struct GemmArgs {
   void* y;
   // launch shape
   int rows_per_wave;    // row tiles of 16 per wavefront: 1, 2 or 4
-  int waves_per_group;  // wavefronts per workgroup: 1..16 (GEMV), 4 (skinny GEMM)
-  int col_tiles;        // 16-column batch tiles per wavefront: 1, 2 or 4
-  int k_splits;         // workgroups splitting the channels (B <= 16 path); > 1 needs workspace
+  int waves_per_group;  // wavefronts per workgroup: 1..16 (GEMV), 4 or 8 (skinny GEMM)
+  int col_tiles;        // 16-column batch tiles per workgroup: 1 (GEMV), 2, 3, 4, 6 or 8 (skinny GEMM)
+  int k_splits;         // workgroups splitting the channels; > 1 needs workspace
   void* workspace;      // float32 [k_splits][B][N] partial sums when k_splits > 1
   int grid_limit;       // B <= 16: cap on the persistent grid (0 = as many as are resident)
   size_t lds_limit;     // B <= 16: LDS a workgroup may use (sizes the per-workgroup result buffer)

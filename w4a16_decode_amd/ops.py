@@ -239,8 +239,8 @@ def gemm_config(x, qw: QuantizedWeight, rows_per_wave: int, waves_per_group: int
                 col_tiles: int | None = None, out=None, workspace=None):
     """q4_gemm_config: q4_gemm with an explicit launch shape (tuning).
 
-    col_tiles defaults to 1 for B <= 16 (GEMV) and to the tiles of 16 rows B needs
-    (2, 4 or 8) for the skinny GEMM."""
+    col_tiles defaults to 1 for B <= 16 (GEMV) and, for the skinny GEMM, to the power of
+    two (2, 4 or 8) of 16-row tiles that covers B; 3 and 6 are accepted too."""
     B, out = _prep_gemm(x, qw, out)
     lib = _lib.load()
     if col_tiles is None:
