@@ -161,7 +161,7 @@ def regret(rows, coef):
     return out
 
 
-def run_grid(out_path: str, shapes, batches) -> None:
+def run_grid(out_path: str, shapes, batches, group: int = 128, asym: bool = False) -> None:
     import torch
 
     sys.path.insert(0, os.path.dirname(HERE))
@@ -192,7 +192,7 @@ def run_grid(out_path: str, shapes, batches) -> None:
     with open(out_path, "w") as out:
         for N, K in shapes:
             copies = min(32, max(2, -(-int(0.6e9) // int(N * K * 0.515625))))
-            qws = [q4.quantize_pack(synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev), 128)
+            qws = [q4.quantize_pack(synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev), group, asym)
                    for c in range(copies)]
             for B in batches:
                 x = synth.device_activation(B, K, seed=4, layer=0, matrix=0, device=dev)
@@ -212,8 +212,10 @@ def run_grid(out_path: str, shapes, batches) -> None:
                     items = list(graphs.items())
                     for k, g in (items if rnd % 2 == 0 else items[::-1]):
                         best[k] = min(best[k], gtime(g) / copies)
-                out.write(json.dumps({"N": N, "K": K, "B": B, "us": {k: round(v * 1e6, 2) for k, v in best.items()}},
-                                     separators=(",", ":")) + "\n")
+                row = {"N": N, "K": K, "B": B, "us": {k: round(v * 1e6, 2) for k, v in best.items()}}
+                if group != 128 or asym:
+                    row.update(group=group, asym=asym)
+                out.write(json.dumps(row, separators=(",", ":")) + "\n")
                 out.flush()
                 print(f"{N}x{K} B={B}: {len(best)} shapes", flush=True)
                 del graphs
@@ -231,10 +233,12 @@ def main(argv=None) -> int:
     g.add_argument("--shapes", default="28672x8192,8192x28672,57344x8192,10240x8192,8192x8192,4096x14336,"
                                         "6144x4096,14336x4096,28672x4096")
     g.add_argument("--batches", default="17,24,32,40,48,56,64,80,96,112,128,144,160,192,224,256")
+    g.add_argument("--group", type=int, default=128)
+    g.add_argument("--asym", action="store_true")
     args = ap.parse_args(argv)
     if args.cmd == "grid":
         shapes = [tuple(map(int, s.split("x"))) for s in args.shapes.split(",")]
-        run_grid(args.out, shapes, [int(b) for b in args.batches.split(",")])
+        run_grid(args.out, shapes, [int(b) for b in args.batches.split(",")], args.group, args.asym)
         return 0
     rows = load(args.grids)
     coef = fit(rows)
