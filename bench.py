@@ -700,7 +700,7 @@ def main(argv=None):
                 "frac": round(k_gbs / perfmodel.HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "measured_read_GBps": round(read_gbs, 1), "frac_of_measured_read": round(k_gbs / read_gbs, 4),
-                "kernel": f"gemv_kernel, fused gate/up {qw0.out_features}x{qw0.in_features}, B=1, g=128",
+                "kernel": f"gemv_burst_kernel, fused gate/up {qw0.out_features}x{qw0.in_features}, B=1, g=128",
                 "avg_us": round(d_avg * 1e6, 3), "bytes_per_launch": kbytes, "launches_timed": n_timed}
     # the same kernel's average duration in the committed rocprofv3 kernel trace of this command
     # (its summary under profiles/, while the kernel sources match): the two must agree

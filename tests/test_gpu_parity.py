@@ -408,3 +408,33 @@ def test_full_fused_gate_up_batches(q4):
 def test_full_heavy_tailed_gemv(q4, g, asym):
     say(f"heavy-tailed GEMV g={g} asym={asym}")
     _full_size_check(q4, 14336, 4096, g, (1,), asym=asym, seed=5, heavy=True)
+
+
+# Staged one-row-tile GEMVs (gemv_burst_kernel): units of one 4-block burst (4096x4096
+# and 6144x4096 at B <= 2, 8 chunks of 32 blocks) and of several (14336x4096 at B = 4).
+# Each wavefront's first units are fixed and the LDS unit counter is read only after
+# the barrier that follows its initialisation; a product that took a unit from an
+# uninitialised counter would skip or repeat units. The products run repeatedly with
+# a skinny GEMM between them (other data left in LDS) and must all give the bits of
+# the first, which must match the oracle.
+@pytest.mark.parametrize("N,K,B", [(4096, 4096, 1), (4096, 4096, 2), (6144, 4096, 1), (14336, 4096, 4)])
+def test_burst_gemv_units_repeatable(q4, N, K, B):
+    import torch
+
+    say(f"burst GEMV N={N} K={K} B={B}")
+    R, W, KS, CT = q4.gemm_shape(B, N, K, 128)
+    assert (R, KS, CT) == (1, 1, 1), (R, W, KS, CT)  # the staged one-row-tile launch
+    W_ = synth.weight(N, K, seed=31)
+    x = synth.activation(B, K, seed=31)
+    qw = q4.quantize_pack(to_gpu(W_), 128)
+    q_o, s_o = oracle.quantize_sym(W_, 128)
+    ref = oracle.gemm_ref(x, oracle.dequant_sym(q_o, s_o, 128))
+    xg = to_gpu(x)
+    other = q4.quantize_pack(to_gpu(synth.weight(1024, 2048, seed=32)), 128)
+    xo = to_gpu(-np.abs(synth.activation(64, 2048, seed=32)))
+    first = q4.gemm(xg, qw)
+    assert_close(to_np(first), ref, f"burst GEMV {N}x{K} B={B}")
+    for _ in range(8):
+        q4.gemm(xo, other)
+        y = q4.gemm(xg, qw)
+        assert torch.equal(y, first), f"burst GEMV {N}x{K} B={B}: a repeated product differs"

@@ -11,7 +11,8 @@ product over every copy, warms the GPU up, and then replays the two graphs in
 alternating order (A B, B A, B A, A B, ...) for the given number of rounds. It prints
 the median time per launch of each build and the median and interquartile range of
 the per-round differences A - B, and flags outputs that differ by more than 1e-3
-relative L2 (two builds that sum in a different order differ at rounding level only).
+relative L2 (two builds that sum in a different order differ at rounding level only),
+and says whether the two outputs are bit-identical.
 
 Interleaving matters on this hardware: the first graph timed after the GPU idles runs
 1-4 us slow, and one kernel's time differs by up to +-1 us from one board to the next,
@@ -104,6 +105,7 @@ def main(argv=None) -> int:
                 warmed = True
             ya, yb = ys["A"].float(), ys["B"].float()
             err = ((ya - yb).norm() / ya.norm().clamp_min(1e-30)).item()
+            same = bool(torch.equal(ys["A"], ys["B"]))
             t = {n: [] for n in libs}
             for r in range(args.rounds):
                 order = ("A", "B") if r % 2 == 0 else ("B", "A")
@@ -112,7 +114,8 @@ def main(argv=None) -> int:
                 for n in order:
                     t[n].append(replay_time(graphs[n]) / copies)
             d = sorted(a - b for a, b in zip(t["A"], t["B"]))
-            flag = f"  !! outputs differ: rel L2 {err:.1e}" if err > 1e-3 else ""
+            flag = f"  !! outputs differ: rel L2 {err:.1e}" if err > 1e-3 else (
+                "  (outputs bit-identical)" if same else f"  (outputs differ at rounding level: rel L2 {err:.1e})")
             print(f"{N}x{K} B={B:3d}: A {statistics.median(t['A']) * 1e6:7.2f}  B {statistics.median(t['B']) * 1e6:7.2f}"
                   f"  A-B {statistics.median(d) * 1e6:+6.2f} [{d[len(d) // 4] * 1e6:+.2f}, "
                   f"{d[(3 * len(d)) // 4] * 1e6:+.2f}] us{flag}", flush=True)

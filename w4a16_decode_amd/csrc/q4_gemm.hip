@@ -111,6 +111,97 @@ __device__ __forceinline__ half8_t magic8_i8(uint32_t d0, uint32_t d1) {
   return __builtin_bit_cast(half8_t, make_uint4(p0, p1, p2, p3));
 }
 
+// Step 1 of the staged GEMVs: the workgroup's x slice (all B rows of the k-split's
+// channels from block wsb0 on) -> registers, XCH chunks of 16 bytes per thread, the
+// fewest that cover it (indices clamped into x, so every thread issues the same
+// number of loads and the later wait is exact).
+template <int XCH>
+__device__ __forceinline__ void gemv_load_x(uint4 (&xr)[XCH], const uint16_t* __restrict__ x, int B, int K, int wsb0,
+                                            int row_chunks) {
+  const int xchunks = B * row_chunks;
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int idx = min((int)threadIdx.x + i * (int)blockDim.x, xchunks - 1);
+    const int b = idx / row_chunks;
+    const int k = min(wsb0 * kSuperK + (idx - b * row_chunks) * 8, K - 8);
+    xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
+  }
+}
+
+// Step 3 of the staged GEMVs: the x slice -> LDS (x rows of xstride = row_chunks * 8
+// + kGemmRowPad halfs; elements 2, 3, 6, 7 of every 8 divided by 16 when BIAS and
+// the codes are INT4: exact powers of two; channels past K are zero), plus the zero
+// row. With BIAS the per-unit bias 1032 * (sum of plain elements) + 1152 * (sum of
+// scaled elements) (INT8 codes: 1152 * sum(x)) is reduced on the way into beta: the
+// UNIT / 8 chunks of a bias unit sit in consecutive lanes (row_chunks is a multiple
+// of 16 and the block a multiple of 64 threads).
+template <int XCH, bool BIAS, bool Q8, int UNIT>
+__device__ __forceinline__ void gemv_store_x(const uint4 (&xr)[XCH], uint16_t* xl, uint16_t* xzero, float* beta, int B,
+                                             int K, int wsb0, int row_chunks, int nunits) {
+  constexpr int CPU = UNIT / 8;  // chunks per bias unit
+  const int xchunks = B * row_chunks;
+  const int xstride = row_chunks * 8 + kGemmRowPad;
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int idx = threadIdx.x + i * blockDim.x;
+    if (i * (int)blockDim.x >= xchunks) break;  // uniform: no chunk of this round is real
+    const bool real = idx < xchunks;
+    const int b = idx / row_chunks;
+    const int c8 = idx - b * row_chunks;
+    uint4 v = (real && wsb0 * kSuperK + c8 * 8 < K) ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
+    if (BIAS) {
+      // INT8 codes keep x as it is: bias 1152 * sum(x) (magic8_i8)
+      half8_t h = as_half8(v);
+      if (!Q8) {
+        h[2] *= (_Float16)0.0625f;
+        h[3] *= (_Float16)0.0625f;
+        h[6] *= (_Float16)0.0625f;
+        h[7] *= (_Float16)0.0625f;
+        v = __builtin_bit_cast(uint4, h);
+      }
+      float plain = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
+      float scaled = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
+#pragma unroll
+      for (int m = 1; m < CPU; m <<= 1) {
+        plain += __shfl_xor(plain, m);
+        scaled += __shfl_xor(scaled, m);
+      }
+      // one explicit fma: the same rounding in every kernel this is inlined into
+      if (real && c8 % CPU == 0)
+        beta[b * nunits + c8 / CPU] = Q8 ? 1152.f * (plain + scaled) : __builtin_fmaf(1032.f, plain, 1152.f * scaled);
+    }
+    if (real) *reinterpret_cast<uint4*>(xl + b * xstride + c8 * 8) = v;
+  }
+  if (threadIdx.x < kSuperK / 8) *reinterpret_cast<uint4*>(xzero + threadIdx.x * 8) = make_uint4(0u, 0u, 0u, 0u);
+  if (BIAS && threadIdx.x == 0) beta[B * nunits] = 0.f;
+}
+
+// Step 4 of the staged GEMVs (after the barrier that ends the streaming): the units'
+// partial sums, parked in LDS as [unit = i * CH + c][r][b][16 rows], added in chunk
+// order for every row block i of the workgroup -> y, or with KS > 1 -> the k-split's
+// float32 slice of the workspace; e = ((i * R + r) * B + b) * 16 + row.
+template <int R>
+__device__ __forceinline__ void gemv_write_units(const float* part0, int n_rb, int CH, int B, int N, int rb_first,
+                                                 int rb_stride, int KS, int ks, uint16_t* __restrict__ y,
+                                                 float* __restrict__ ws) {
+  const int nout = n_rb * R * 16 * B;
+  for (int e = threadIdx.x; e < nout; e += blockDim.x) {
+    const int row = e & 15;
+    const int t = e >> 4;
+    const int b = t % B;
+    const int ir = t / B;  // i * R + r
+    const int i = ir / R, r = ir - i * R;
+    const float* pp = part0 + ((size_t)i * CH * R + r) * 16 * B + b * 16 + row;
+    float sum = 0.f;
+    for (int c = 0; c < CH; ++c) sum += pp[(size_t)c * R * 16 * B];
+    const int n = ((rb_first + i * rb_stride) * R + r) * 16 + row;
+    if (n < N) {
+      if (KS == 1) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+      else ws[((size_t)ks * B + b) * N + n] = sum;
+    }
+  }
+}
+
 // Q8: W8A16 codes (per-row INT8 scale passed as one group spanning the row, J = S,
 // Gp = 1): a 16-row x 128-channel block is 2 KiB, two 1 KiB halves of 64 channels;
 // lane l's 16 bytes of half h hold row l%16, channels 64h + 32j + 8(l/16) + e at
@@ -157,19 +248,10 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
   const int arow = lane & 15;
   const int bcol = lane & 15;
 
-  // 1. the workgroup's x slice -> registers: XCH chunks of 16 bytes per thread, the
-  //    fewest that cover it (indices clamped into x, so every thread issues the same
-  //    number of loads and the later wait is exact)
+  // 1. the workgroup's x slice -> registers
   const int row_chunks = KR >> 3;
-  const int xchunks = B * row_chunks;
   uint4 xr[XCH];
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int idx = min((int)threadIdx.x + i * (int)blockDim.x, xchunks - 1);
-    const int b = idx / row_chunks;
-    const int k = min(wsb0 * kSuperK + (idx - b * row_chunks) * 8, K - 8);
-    xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)b * K + k);
-  }
+  gemv_load_x(xr, x, B, K, wsb0, row_chunks);
   // 2. the first L blocks of codes / scales (P/2 in the burst ring, else P-1).
   //    Those loads end at most L / (shortest unit) units, so the first KST grabs of
   //    each wavefront, which cover them, take units wave + j * W (j < KST) without
@@ -253,44 +335,8 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
 #pragma unroll
   for (int p = 0; p < L; ++p) load(buf[p]);
 
-  // 3. x slice -> LDS (elements 2, 3, 6, 7 of every 8 divided by 16 when BIAS: exact
-  //    powers of two; channels past K are zero), plus the zero row. With BIAS the
-  //    per-unit bias 1032 * (sum of plain elements) + 1152 * (sum of scaled elements)
-  //    is reduced on the way: the UNIT / 8 chunks of a bias unit sit in consecutive
-  //    lanes (row_chunks is a multiple of 16 and the block a multiple of 64 threads).
-  constexpr int CPU = UNIT / 8;  // chunks per bias unit
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int idx = threadIdx.x + i * blockDim.x;
-    if (i * (int)blockDim.x >= xchunks) break;  // uniform: no chunk of this round is real
-    const bool real = idx < xchunks;
-    const int b = idx / row_chunks;
-    const int c8 = idx - b * row_chunks;
-    uint4 v = (real && wsb0 * kSuperK + c8 * 8 < K) ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
-    if (BIAS) {
-      // INT8 codes keep x as it is: bias 1152 * sum(x) (magic8_i8)
-      half8_t h = as_half8(v);
-      if (!Q8) {
-        h[2] *= (_Float16)0.0625f;
-        h[3] *= (_Float16)0.0625f;
-        h[6] *= (_Float16)0.0625f;
-        h[7] *= (_Float16)0.0625f;
-        v = __builtin_bit_cast(uint4, h);
-      }
-      float plain = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
-      float scaled = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
-#pragma unroll
-      for (int m = 1; m < CPU; m <<= 1) {
-        plain += __shfl_xor(plain, m);
-        scaled += __shfl_xor(scaled, m);
-      }
-      if (real && c8 % CPU == 0)
-        beta[b * nunits + c8 / CPU] = Q8 ? 1152.f * (plain + scaled) : 1032.f * plain + 1152.f * scaled;
-    }
-    if (real) *reinterpret_cast<uint4*>(xl + b * xstride + c8 * 8) = v;
-  }
-  if (threadIdx.x < kSuperK / 8) *reinterpret_cast<uint4*>(xzero + threadIdx.x * 8) = make_uint4(0u, 0u, 0u, 0u);
-  if (BIAS && threadIdx.x == 0) beta[B * nunits] = 0.f;
+  // 3. x slice -> LDS, plus the zero row (and, with BIAS, the per-unit biases)
+  gemv_store_x<XCH, BIAS, Q8, UNIT>(xr, xl, xzero, beta, B, K, wsb0, row_chunks, nunits);
   lds_barrier();
 
   float4_t acc[R];
@@ -397,25 +443,195 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
     }
   }
 
-  // 4. results of all row blocks: the units' partials added in chunk order -> y
-  //    (or the k-split workspace); e = ((i * R + r) * B + b) * 16 + row
+  // 4. results of all row blocks -> y (or the k-split workspace)
   lds_barrier();
-  const int nout = n_rb * R * 16 * B;
-  for (int e = threadIdx.x; e < nout; e += blockDim.x) {
-    const int row = e & 15;
-    const int t = e >> 4;
-    const int b = t % B;
-    const int ir = t / B;  // i * R + r
-    const int i = ir / R, r = ir - i * R;
-    const float* pp = part0 + ((size_t)i * CH * R + r) * 16 * B + b * 16 + row;
-    float sum = 0.f;
-    for (int c = 0; c < CH; ++c) sum += pp[(size_t)c * R * 16 * B];
-    const int n = ((rb_first + i * rb_stride) * R + r) * 16 + row;
-    if (n < N) {
-      if (KS == 1) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
-      else ws[((size_t)ks * B + b) * N + n] = sum;
-    }
+  gemv_write_units<R>(part0, n_rb, CH, B, N, rb_first, rb_stride, KS, ks, y, ws);
+}
+
+// ---------------------------------------------------------------------------------
+// GEMV for the common case of the staged kernel: symmetric INT4 codes with one scale
+// per 1 KiB block (groups of 128 channels), one row tile per wavefront, and chunks of
+// a whole number of 4-block bursts (the host checks S % KS == 0 and
+// (S / KS) % (4 CH) == 0). It runs gemv_kernel<1, 1, false, 8, XCH>'s grid, units,
+// x staging, burst ring (two halves of 4 blocks), arithmetic and final reduction, so
+// the two give identical bits; what differs is the instruction stream around the
+// loads. gemv_kernel re-derives every block's code and scale addresses from a block
+// index, with clamps, a group division and a unit test per block (~40 scalar
+// instructions and several branches per 1 KiB block). Here a unit's code and scale
+// bases are formed once when the unit is taken, a burst is 4 loads from one scalar
+// base plus per-lane offsets held in registers (block q of a burst sits q * CH KiB
+// further), and the unit counter is read once per unit.
+template <int XCH>
+__global__ __launch_bounds__(16 * 64)
+void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
+                       const uint16_t* __restrict__ scales, int N, int K, int S, int Gp, int KS, int nRB, int CH,
+                       uint16_t* __restrict__ y, float* __restrict__ ws) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NB = 4;  // blocks per burst
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ks = blockIdx.x % KS;
+  const int rb_first = blockIdx.x / KS;
+  const int rb_stride = gridDim.x / KS;
+  const int nsb = S / KS;  // blocks per split: a multiple of NB * CH
+  const int wsb0 = nsb * ks;
+  const int bursts = nsb / (NB * CH);  // bursts per unit
+  const int n_rb = rb_first < nRB ? (nRB - 1 - rb_first) / rb_stride + 1 : 0;
+  const int n_units = n_rb * CH;
+  const int KR = nsb * kSuperK;
+  const int xstride = KR + kGemmRowPad;
+  const GemvLds lay(B, nsb, 1, true, 1, n_units);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* xzero = xl + B * xstride;
+  float* beta = reinterpret_cast<float*>(smem + lay.x);
+  float* part0 = reinterpret_cast<float*>(smem + lay.x + lay.beta);  // [unit][b][16 rows]
+  int* counter = reinterpret_cast<int*>(smem + lay.x + lay.beta + lay.part);
+  const int crow = 4 * (lane >> 4);
+  const int bcol = lane & 15;
+
+  // 1. the workgroup's x slice -> registers
+  const int row_chunks = KR >> 3;
+  uint4 xr[XCH];
+  gemv_load_x(xr, x, B, K, wsb0, row_chunks);
+
+  // The wavefront's cursor (all uniform): the unit it streams (-1 once the units
+  // have run out), that unit's chunk, its code and scale bases (block wsb0 + c of
+  // its tile) and the next burst to load. Block q of burst j of a unit sits
+  // (j * NB + q) * CH blocks past the unit's base: the lane offsets of the NB blocks
+  // of a burst are fixed registers, the burst's scalar base moves by NB * CH blocks.
+  const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
+  const unsigned char* sk = reinterpret_cast<const unsigned char*>(scales);
+  const uint32_t cstride = (uint32_t)CH * 1024u;  // bytes between a unit's blocks (codes)
+  const uint32_t sstride = (uint32_t)CH * 32u;    // ... (scales: 16 float16 per block)
+  uint32_t woff[NB], soff[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    woff[q] = (uint32_t)lane * 16u + q * cstride;
+    soff[q] = (uint32_t)crow * 2u + q * sstride;
   }
+  int c_unit = -1, c_chunk = 0, c_burst = 0;
+  const unsigned char* c_w = pk;
+  const unsigned char* c_s = sk;
+  // Units: the first KST of each wavefront are fixed (wave, wave + W): they cover
+  // the burst issued before the barrier that publishes x (with one-burst units that
+  // burst ends the first unit and takes the second). Later units come from the
+  // counter (every lane adds 1, so a grab moves it by 64), which thread 0 sets
+  // before that barrier and nobody touches until after it.
+  const int KST = bursts == 1 ? 2 : 1;
+  int grabs = 0;
+  auto take = [&]() __attribute__((always_inline)) {
+    const int u = grabs < KST ? wave + grabs * W : __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;
+    ++grabs;
+    c_burst = 0;
+    if ((unsigned)u >= (unsigned)n_units) {
+      c_unit = -1;  // the bases keep the last unit: later loads stay in bounds
+      return;
+    }
+    c_unit = u;
+    const int i = u / CH;
+    c_chunk = u - i * CH;
+    const size_t tile = (size_t)(rb_first + i * rb_stride);
+    c_w = pk + (tile * S + wsb0 + c_chunk) * 1024;
+    c_s = sk + (tile * Gp + wsb0 + c_chunk) * 32;
+  };
+  if (threadIdx.x == 0) *counter = KST * W * 64;
+  take();
+
+  // one burst in flight: codes and scales of NB blocks, the unit and chunk they
+  // belong to, the index of the burst's first block in the unit and whether it ends it
+  struct Burst {
+    uint4 w[NB];
+    uint2 sc[NB];
+    int unit, chunk, j0;
+    bool last;
+  };
+  auto issue = [&](Burst& b) __attribute__((always_inline)) {
+    const size_t boff = (size_t)c_burst * NB * CH;
+    const unsigned char* wb = c_w + boff * 1024;
+    const unsigned char* sb = c_s + boff * 32;
+    // codes and scale of one block after the other: loads complete in order, so
+    // block q waits for the first 2 (q + 1) loads of the burst only
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      b.w[q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb + woff[q])));
+      b.sc[q] = *reinterpret_cast<const uint2*>(sb + soff[q]);
+    }
+    b.unit = c_unit;
+    b.chunk = c_chunk;
+    b.j0 = c_burst * NB;
+    b.last = c_burst + 1 == bursts;
+    if (c_unit < 0) return;
+    if (++c_burst == bursts) take();
+  };
+  Burst ring[2];
+  issue(ring[0]);
+
+  // 3. x slice -> LDS, plus the zero row and the per-unit biases
+  const int nunits = nsb;
+  gemv_store_x<XCH, true, false, kSuperK>(xr, xl, xzero, beta, B, K, wsb0, row_chunks, nunits);
+  lds_barrier();
+
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const DequantRegs dq = DequantRegs::make();
+  // LDS read pointers of this lane's activation operand and bias; lanes of absent
+  // batch rows stay on the zero row / zero bias (steps of 0)
+  const bool real_col = bcol < B;
+  const uint16_t* xlane0 = real_col ? xl + bcol * xstride + 8 * (lane >> 4) : xzero + 8 * (lane >> 4);
+  const float* blane0 = real_col ? beta + bcol * nunits : beta + B * nunits;
+  // activation operands and bias of the next block to compute, read from LDS one
+  // block ahead; block index sb = s - wsb0 = chunk + j * CH (uniform: the lane's
+  // offset is a select, not a multiply)
+  half8_t xb[4];
+  float bu;
+  auto read_x = [&](int sb) __attribute__((always_inline)) {
+    const uint16_t* xp = xlane0 + (real_col ? sb * kSuperK : 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xb[m] = *reinterpret_cast<const half8_t*>(xp + m * kBlockK);
+    bu = blane0[real_col ? sb : 0];
+  };
+  auto block_of = [&](const Burst& b, int q) __attribute__((always_inline)) {
+    return b.unit < 0 ? 0 : b.chunk + (b.j0 + q) * CH;
+  };
+  read_x(block_of(ring[0], 0));
+
+  // the NB blocks of burst b, each: 4 MFMA steps over the raw magic-number operands,
+  // bias removed and the group's scale applied in float32; nx is the burst after it
+  // (whose first block's x is read ahead during b's last block)
+  auto compute = [&](const Burst& b, const Burst& nx) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      half8_t xc[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xc[m] = xb[m];
+      const float bc = bu;
+      read_x(q + 1 < NB ? block_of(b, q + 1) : block_of(nx, 0));
+      const half4_t sh = __builtin_bit_cast(half4_t, b.sc[q]);
+      float4_t part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) part = mfma16x16x32(magic8r(lane_dword(b.w[q], mm), dq), xc[mm], part);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)sh[i], part[i] - bc, acc[i]);
+    }
+    if (!b.last) return;
+    // unit finished: park the partial sums of the real batch columns (the lane
+    // holds rows crow..crow+3 of column bcol) and start the next unit from zero
+    if (real_col) *reinterpret_cast<float4_t*>(part0 + (size_t)b.unit * 16 * B + bcol * 16 + crow) = acc;
+    acc = float4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // once a burst has no unit, every later one has none either
+  while (ring[0].unit >= 0) {
+    issue(ring[1]);
+    compute(ring[0], ring[1]);
+    issue(ring[0]);
+    if (ring[1].unit < 0) break;
+    compute(ring[1], ring[0]);
+  }
+
+  // 4. results of all row blocks -> y (or the k-split workspace)
+  lds_barrier();
+  gemv_write_units<1>(part0, n_rb, CH, B, N, rb_first, rb_stride, KS, ks, y, ws);
 }
 
 __global__ void reduce_splits_kernel(const float* __restrict__ ws, int KS, int64_t BN, uint16_t* __restrict__ y) {
@@ -767,7 +983,11 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   const int nRB = (T + R - 1) / R;
   const int max_nsb = (S + KS - 1) / KS;
   const int min_nsb = S / KS;  // >= 1: the host keeps KS <= S
-  const void* fn = reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>);
+  // the burst kernel where its conditions hold (same grid, units and result bits)
+  constexpr bool kBurstKind = R == 1 && GSUB == 1 && !ASYM && !Q8;
+  const bool burst = kBurstKind && J == 1 && S % KS == 0;  // CH is checked below
+  const void* fn = burst ? reinterpret_cast<const void*>(&gemv_burst_kernel<XCH>)
+                         : reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>);
   const size_t lim = a.lds_limit;
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, 0).total;
@@ -794,6 +1014,18 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   CH = std::max(CH, 1);
   const size_t lds = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, n_rb * CH).total;
   const int grid = (int)(per_split * KS);
+  if constexpr (kBurstKind) {
+    if (burst && (S / KS) % (4 * CH) == 0) {
+      hipLaunchKernelGGL((gemv_burst_kernel<XCH>), dim3(grid), dim3(W * kWave), lds, stream,
+                         static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
+                         static_cast<const uint16_t*>(a.scales), a.N, a.K, S, a.Gp, KS, nRB, CH,
+                         static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
+      if (KS > 1)
+        launch_reduce_splits(static_cast<const float*>(a.workspace), KS, (int64_t)a.B * a.N,
+                             static_cast<uint16_t*>(a.y), stream);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>), dim3(grid), dim3(W * kWave), lds, stream,
                      static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
