@@ -504,11 +504,13 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
   const unsigned char* sk = reinterpret_cast<const unsigned char*>(scales);
   const uint32_t cstride = (uint32_t)CH * 1024u;  // bytes between a unit's blocks (codes)
   const uint32_t sstride = (uint32_t)CH * 32u;    // ... (scales: 16 float16 per block)
-  uint32_t woff[NB], soff[NB];
+  uint32_t woff[NB], soff[NB], lw[NB], ls[NB];  // lw, ls: the offsets loads use now
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     woff[q] = (uint32_t)lane * 16u + q * cstride;
     soff[q] = (uint32_t)crow * 2u + q * sstride;
+    lw[q] = woff[q];
+    ls[q] = soff[q];
   }
   int c_unit = -1, c_chunk = 0, c_burst = 0;
   const unsigned char* c_w = pk;
@@ -525,7 +527,19 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
     ++grabs;
     c_burst = 0;
     if ((unsigned)u >= (unsigned)n_units) {
-      c_unit = -1;  // the bases keep the last unit: later loads stay in bounds
+      // no more units: the loads that still follow (unconditional, so the compiler
+      // keeps exact vmcnt counts) all re-read the block this wavefront loaded last,
+      // which the L2 still holds or is fetching. Re-reading the last unit's first
+      // burst, loaded long before, fetched 4 KiB more per wavefront from HBM (+6%
+      // bytes on gate/up); its last whole burst still +4% (+17% on q/k/v); one burst
+      // shared by all such wavefronts cost ~0.8 us on the small matrices.
+      c_unit = -1;
+      c_burst = bursts - 1;
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        lw[q] = woff[NB - 1];
+        ls[q] = soff[NB - 1];
+      }
       return;
     }
     c_unit = u;
@@ -554,8 +568,8 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
     // block q waits for the first 2 (q + 1) loads of the burst only
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      b.w[q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb + woff[q])));
-      b.sc[q] = *reinterpret_cast<const uint2*>(sb + soff[q]);
+      b.w[q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb + lw[q])));
+      b.sc[q] = *reinterpret_cast<const uint2*>(sb + ls[q]);
     }
     b.unit = c_unit;
     b.chunk = c_chunk;
