@@ -875,7 +875,8 @@ void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __re
             plain += __shfl_xor(plain, m);
             scaled += __shfl_xor(scaled, m);
           }
-          if (c8 % CPU == 0) bw[b * kUnitBlocks * GSUB + c8 / CPU] = 1032.f * plain + 1152.f * scaled;
+          // one explicit fma, as in every GEMV: the same rounding wherever it is inlined
+          if (c8 % CPU == 0) bw[b * kUnitBlocks * GSUB + c8 / CPU] = __builtin_fmaf(1032.f, plain, 1152.f * scaled);
         }
         *reinterpret_cast<uint4*>(xw + b * kUnitXStride + 8 * c8) = v;
       }
@@ -969,19 +970,249 @@ void gemv_stream_kernel(const uint16_t* __restrict__ x, int B, const uint4* __re
 
   // results: the units' partials added in chunk order -> y
   lds_barrier();
-  const int nout = n_rb * R * 16 * B;
-  for (int e = threadIdx.x; e < nout; e += blockDim.x) {
-    const int row = e & 15;
-    const int t = e >> 4;
-    const int b = t % B;
-    const int ir = t / B;  // i * R + r
-    const int i = ir / R, r = ir - i * R;
-    const float* pp = part0 + ((size_t)i * CH * R + r) * 16 * B + b * 16 + row;
-    float sum = 0.f;
-    for (int c = 0; c < CH; ++c) sum += pp[(size_t)c * R * 16 * B];
-    const int n = ((rb_first + i * rb_stride) * R + r) * 16 + row;
-    if (n < N) y[(size_t)b * N + n] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  gemv_write_units<R>(part0, n_rb, CH, B, N, rb_first, rb_stride, 1, 0, y, nullptr);
+}
+
+// ---------------------------------------------------------------------------------
+// The streaming GEMV for its common case: symmetric INT4 codes with one scale per
+// block (groups of 128 channels), two row tiles per wavefront. Same grid, units
+// (8 strided blocks), per-unit activation loads and LDS slices, arithmetic and final
+// reduction as gemv_stream_kernel<2, 1, false, 4, BMAX>, so the two give identical
+// bits; the instruction stream around the loads is that of gemv_burst_kernel. The
+// weights of a unit go in 4 bursts of 2 blocks (each block: both row tiles' codes
+// and scales), two bursts in flight: a unit's 2 x 2 tile bases are formed once
+// when it is taken, the 2 blocks of a burst (CH KiB apart) are loads from those
+// scalar bases plus lane offsets held in registers, and the counter is read once
+// per unit. The unit's x loads go out when it is taken, right before its first
+// codes; the x of the next unit replaces this one's in the wavefront's LDS slice when
+// this unit's last block is computed (4 bursts per unit, 2 in flight: the next unit
+// is taken only after that). It holds more registers than 128 (one 8-wavefront
+// workgroup per CU), so the host runs it where the grid needs no more than that.
+template <int BMAX>
+__global__ __launch_bounds__(512)
+void gemv_stream_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
+                              const uint16_t* __restrict__ scales, int N, int K, int T, int S, int Gp, int nRB,
+                              uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int R = 2;                        // row tiles per wavefront
+  constexpr int NB = 2;                       // blocks per burst
+  constexpr int BURSTS = kUnitBlocks / NB;    // bursts per unit
+  constexpr int CPU = kSuperK / 8;            // 16-byte chunks per bias unit (one block)
+  static_assert(BURSTS >= 2, "the next unit is taken only after this one's last block is computed");
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int rb_first = blockIdx.x;
+  const int rb_stride = gridDim.x;
+  const int CH = S / kUnitBlocks;  // the host keeps S a multiple of 8
+  const int n_rb = rb_first < nRB ? (nRB - 1 - rb_first) / rb_stride + 1 : 0;
+  const int n_units = n_rb * CH;
+  const GemvStreamLds lay(BMAX, 1, true, W, R, B, n_units);
+  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + (size_t)wave * BMAX * kUnitXStride;
+  float* bw = reinterpret_cast<float*>(smem + lay.xw) + (size_t)wave * BMAX * kUnitBlocks;
+  uint16_t* xzero = reinterpret_cast<uint16_t*>(smem + lay.xw + lay.bw);
+  float* bzero = reinterpret_cast<float*>(smem + lay.xw + lay.bw + kSuperK * 2);
+  float* part0 = reinterpret_cast<float*>(smem + lay.xw + lay.bw + lay.zero);  // [unit][r][b][16 rows]
+  int* counter = reinterpret_cast<int*>(smem + lay.xw + lay.bw + lay.zero + lay.part);
+  const int crow = 4 * (lane >> 4);
+  const int bcol = lane & 15;
+  const int kq = lane >> 4;
+
+  // the zero row and the counter are published by the barrier after the first
+  // burst; each wavefront's first unit is fixed (unit `wave`: a unit is 4 bursts, so
+  // the one burst issued before that barrier never ends it), later ones come from the
+  // counter, read only after the barrier
+  if (threadIdx.x < kSuperK / 8) *reinterpret_cast<uint4*>(xzero + threadIdx.x * 8) = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) {
+    *bzero = 0.f;
+    *counter = W * 64;
   }
+
+  const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
+  const unsigned char* sk = reinterpret_cast<const unsigned char*>(scales);
+  const uint32_t cstride = (uint32_t)CH * 1024u;  // bytes between a unit's blocks (codes)
+  const uint32_t sstride = (uint32_t)CH * 32u;    // ... (scales)
+  uint32_t woff[NB], soff[NB], lw[NB], ls[NB];  // lane offsets of a burst's blocks; lw, ls: those loads use now
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    woff[q] = (uint32_t)lane * 16u + q * cstride;
+    soff[q] = (uint32_t)crow * 2u + q * sstride;
+    lw[q] = woff[q];
+    ls[q] = soff[q];
+  }
+  // cursor (uniform): unit being streamed (-1 once they have run out), its chunk,
+  // the code and scale bases of its two tiles (block c of each), the next burst
+  int c_unit = -1, c_chunk = 0, c_burst = 0;
+  const unsigned char* c_w[R] = {pk, pk};
+  const unsigned char* c_s[R] = {sk, sk};
+  uint4 xn[BMAX][2];  // x of the unit taken last: channels 8 * (lane + 64 i) of its 1024, per batch row
+  bool first = true;
+  auto take = [&]() __attribute__((always_inline)) {
+    const int u = first ? wave : __builtin_amdgcn_readfirstlane(atomicAdd(counter, 1)) >> 6;
+    first = false;
+    c_burst = 0;
+    if ((unsigned)u < (unsigned)n_units) {
+      c_unit = u;
+      const int i = u / CH;
+      c_chunk = u - i * CH;
+      const int rb = rb_first + i * rb_stride;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const size_t tile = (size_t)min(rb * R + r, T - 1);
+        c_w[r] = pk + (tile * S + c_chunk) * 1024;
+        c_s[r] = sk + (tile * Gp + c_chunk) * 32;
+      }
+    } else {
+      // no more units: the loads that still follow (unconditional, for exact vmcnt
+      // counts) all re-read the block loaded last (still in the L2 or on its way; the
+      // last whole burst cost 4-5% more HBM bytes on down and o), and the x loads
+      // repeat the last unit's
+      c_unit = -1;
+      c_burst = BURSTS - 1;
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        lw[q] = woff[NB - 1];
+        ls[q] = soff[NB - 1];
+      }
+    }
+    // the unit's activations, ahead of its codes (issued on every take, so the
+    // number of loads in flight does not depend on the outcome)
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int pc = lane + 64 * i;  // 16-byte piece pc of the unit: block pc / 16
+        const int k = min((c_chunk + (pc >> 4) * CH) * kSuperK + 8 * (pc & 15), K - 8);
+        xn[b][i] = *reinterpret_cast<const uint4*>(x + (size_t)min(b, B - 1) * K + k);
+      }
+  };
+
+  struct Burst {
+    uint4 w[NB][R];
+    uint2 sc[NB][R];
+    int unit, j0;
+    bool last;
+  };
+  auto issue = [&](Burst& bt) __attribute__((always_inline)) {
+    const size_t boff = (size_t)c_burst * NB * CH;
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        bt.w[q][r] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(c_w[r] + boff * 1024 + lw[q])));
+        bt.sc[q][r] = *reinterpret_cast<const uint2*>(c_s[r] + boff * 32 + ls[q]);
+      }
+    bt.unit = c_unit;
+    bt.j0 = c_burst * NB;
+    bt.last = c_burst + 1 == BURSTS;
+    if (c_unit < 0) return;
+    if (++c_burst == BURSTS) take();
+  };
+
+  // the unit's x (x/16 at elements 2, 3, 6, 7; channels past K are zero) -> this
+  // wavefront's LDS, with the per-block biases 1032 * sum(plain) + 1152 * sum(scaled)
+  // reduced over the 16 lanes of each block
+  int xn_chunk = 0;  // chunk of the unit whose x is in xn
+  auto write_x = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+      if (b >= B) break;  // uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c8 = lane + 64 * i;  // 16-byte chunk of the unit's 1024 channels
+        uint4 v = ((xn_chunk + (c8 >> 4) * CH) * kSuperK + 8 * (c8 & 15) < K) ? xn[b][i] : make_uint4(0u, 0u, 0u, 0u);
+        half8_t h = as_half8(v);
+        h[2] *= (_Float16)0.0625f;
+        h[3] *= (_Float16)0.0625f;
+        h[6] *= (_Float16)0.0625f;
+        h[7] *= (_Float16)0.0625f;
+        v = __builtin_bit_cast(uint4, h);
+        float plain = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
+        float scaled = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
+#pragma unroll
+        for (int m = 1; m < CPU; m <<= 1) {
+          plain += __shfl_xor(plain, m);
+          scaled += __shfl_xor(scaled, m);
+        }
+        if (c8 % CPU == 0) bw[b * kUnitBlocks + c8 / CPU] = __builtin_fmaf(1032.f, plain, 1152.f * scaled);
+        *reinterpret_cast<uint4*>(xw + b * kUnitXStride + 8 * c8) = v;
+      }
+    }
+  };
+
+  take();
+  xn_chunk = c_chunk;
+  Burst ring[2];
+  issue(ring[0]);
+  lds_barrier();  // the zero row and the counter (written above) are set
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const DequantRegs dq = DequantRegs::make();
+  const bool real_col = bcol < B;
+  const uint16_t* xlane0 = real_col ? xw + bcol * kUnitXStride + 8 * kq : xzero + 8 * kq;
+  const float* blane0 = real_col ? bw + bcol * kUnitBlocks : bzero;
+  half8_t xb[4];
+  float bu;
+  auto read_x = [&](int j) __attribute__((always_inline)) {  // block j of the unit in LDS
+    const uint16_t* xp = xlane0 + (real_col ? j * kSuperK : 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xb[m] = *reinterpret_cast<const half8_t*>(xp + m * kBlockK);
+    bu = blane0[real_col ? j : 0];
+  };
+  if (ring[0].unit >= 0) write_x();  // the first unit's x (its loads are the oldest in flight)
+  read_x(0);
+
+  auto compute = [&](const Burst& bt, const Burst& nx) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      half8_t xc[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xc[m] = xb[m];
+      const float bc = bu;
+      const bool last = bt.last && q + 1 == NB;
+      if (!last) read_x(bt.j0 + q + 1);  // same unit: its x is in LDS already
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const half4_t sh = __builtin_bit_cast(half4_t, bt.sc[q][r]);
+        float4_t part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) part = mfma16x16x32(magic8r(lane_dword(bt.w[q][r], mm), dq), xc[mm], part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf((float)sh[i], part[i] - bc, acc[r][i]);
+      }
+      if (!last) continue;
+      if (real_col) {
+        float* pp = part0 + (size_t)bt.unit * R * 16 * B + bcol * 16 + crow;
+#pragma unroll
+        for (int r = 0; r < R; ++r) *reinterpret_cast<float4_t*>(pp + r * 16 * B) = acc[r];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+      // the next unit: its x replaces this one's in LDS (this unit's reads of it were
+      // issued earlier by this wavefront, and LDS serves them in order)
+      if (nx.unit >= 0) {
+        xn_chunk = nx.unit - (nx.unit / CH) * CH;
+        write_x();
+      }
+      read_x(0);
+    }
+  };
+
+  // once a burst has no unit, every later one has none either
+  while (ring[0].unit >= 0) {
+    issue(ring[1]);
+    compute(ring[0], ring[1]);
+    issue(ring[0]);
+    if (ring[1].unit < 0) break;
+    compute(ring[1], ring[0]);
+  }
+
+  // results: the units' partials added in chunk order -> y
+  lds_barrier();
+  gemv_write_units<R>(part0, n_rb, CH, B, N, rb_first, rb_stride, 1, 0, y, nullptr);
 }
 
 template <int R, int GSUB, bool ASYM, int XCH, bool Q8 = false>
@@ -1083,7 +1314,11 @@ hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
   const int W = std::min(a.waves_per_group, 8);
   const int nRB = (T + R - 1) / R;
   const int CH = S / kUnitBlocks;
-  const void* fn = reinterpret_cast<const void*>(&gemv_stream_kernel<R, GSUB, ASYM, P, BMAX>);
+  // the burst form where its conditions hold (same grid, units and result bits)
+  constexpr bool kBurstKind = R == 2 && GSUB == 1 && !ASYM;
+  const bool burst = kBurstKind && J == 1 && nRB <= device_cu_count_cached();  // <= 1 workgroup per CU
+  const void* fn = burst ? reinterpret_cast<const void*>(&gemv_stream_burst_kernel<BMAX>)
+                         : reinterpret_cast<const void*>(&gemv_stream_kernel<R, GSUB, ASYM, P, BMAX>);
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, 0).total;
   const size_t lim = std::max(a.lds_limit, base + unit_bytes * CH);
@@ -1095,6 +1330,15 @@ hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
   if (n_rb > max_rb) grid = (nRB + max_rb - 1) / max_rb;
   n_rb = (int)((nRB + grid - 1) / grid);
   const size_t lds = GemvStreamLds(BMAX, GSUB, !ASYM, W, R, a.B, n_rb * CH).total;
+  if constexpr (kBurstKind) {
+    if (burst) {
+      hipLaunchKernelGGL((gemv_stream_burst_kernel<BMAX>), dim3((unsigned)grid), dim3(W * kWave), lds, stream,
+                         static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
+                         static_cast<const uint16_t*>(a.scales), a.N, a.K, T, S, a.Gp, nRB,
+                         static_cast<uint16_t*>(a.y));
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemv_stream_kernel<R, GSUB, ASYM, P, BMAX>), dim3((unsigned)grid), dim3(W * kWave), lds,
                      stream, static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                      static_cast<const uint16_t*>(a.scales), static_cast<const uint8_t*>(a.zeros), a.N, a.K, T, S,
