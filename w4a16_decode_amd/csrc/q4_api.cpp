@@ -212,13 +212,15 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     int KS = 1;
     // two row tiles per wavefront at B <= 3 stream x per unit (no activation slice
     // to fit in LDS, so no channel split); otherwise the fewest splits whose slice fits
-    const bool streamed = !a->q8 && q4::gemv_streams_x(B, d.Kp, R, 1);
+    const bool streamed =
+        !a->q8 && q4::gemv_streams_x(B, d.Kp, R, 1,
+                                     q4::gemv_stream_burst_ok(d.Np, d.group, a->asym, a->q8, q4::device_cu_count_cached()));
     while (!streamed && KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
     a->rows_per_wave = R;
     a->waves_per_group = W;
     a->k_splits = KS;
     a->lds_limit = lim;
-    if (B >= 4 && !a->q8 && !a->asym && d.group >= 128) {
+    if (B >= 4 && !streamed && !a->q8 && !a->asym && d.group >= 128) {
       // the shape of lowest modelled time (gemv_model_us); ties keep fewer splits
       const int cus = q4::device_cu_count_cached();
       double best = 1e30;
@@ -395,14 +397,25 @@ size_t q4_groups_count(int64_t out, int64_t in, int32_t group) {
   return (size_t)d.Np * (size_t)d.Gp;
 }
 
+// The larger of the split workspaces q4_gemm and q4_gemm_asym need: the two may pick
+// different launch shapes (symmetric codes stream x at B = 4 where asymmetric ones split).
+static size_t splits_workspace_any(int64_t B, const Dims& d) {
+  size_t need = 0;
+  for (bool asym : {false, true}) {
+    q4::GemmArgs a{};
+    a.B = (int)B;
+    a.N = d.N;
+    a.asym = asym;
+    pick_shape((int)B, d, &a);
+    need = std::max(need, splits_workspace(a));
+  }
+  return need;
+}
+
 size_t q4_workspace_bytes(int64_t B, int64_t out, int64_t in, int32_t group) {
   Dims d;
   if (B <= 0 || B >= kMaxDim || check_dims(out, in, group, &d) != Q4_OK) return 0;
-  q4::GemmArgs a{};
-  a.B = (int)B;
-  a.N = d.N;
-  pick_shape((int)B, d, &a);
-  return splits_workspace(a);
+  return splits_workspace_any(B, d);
 }
 
 q4_status q4_gemm_shape(int64_t B, int64_t out, int64_t in, int32_t group, int32_t* shape) {
@@ -493,7 +506,9 @@ static q4_status gemm_common(const void* x, int64_t B, const void* packed, const
       if (col_tiles != 1) return fail(Q4_ERR_UNSUPPORTED, "col_tiles must be 1 for B <= 16");
       a.lds_limit = lds_per_block();
       // the streaming kernel (two row tiles, B <= 3, no split) stages no activation slice
-      const bool streamed = q4::gemv_streams_x((int)B, d.Kp, rows_per_wave, k_splits);
+      const bool streamed = q4::gemv_streams_x(
+          (int)B, d.Kp, rows_per_wave, k_splits,
+          q4::gemv_stream_burst_ok(d.Np, d.group, asym != 0, false, q4::device_cu_count_cached()));
       if (!streamed &&
           !gemv_shape_ok((int)B, d.Kp / 128, k_splits, waves_per_group, rows_per_wave, d.group, asym, a.lds_limit))
         return fail(Q4_ERR_UNSUPPORTED, "k_splits=%d, waves_per_group=%d: more splits than 128-channel blocks, "
@@ -598,11 +613,7 @@ q4_status q4_quantize_pack_perm(const void* W, int64_t out, int64_t in, int32_t 
 size_t q4_workspace_bytes_perm(int64_t B, int64_t out, int64_t in, int32_t group) {
   Dims d;
   if (B <= 0 || B >= kMaxDim || check_dims(out, in, group, &d) != Q4_OK) return 0;
-  q4::GemmArgs a{};
-  a.B = (int)B;
-  a.N = d.N;
-  pick_shape((int)B, d, &a);
-  return splits_workspace(a) + perm_x_bytes(B, in);
+  return splits_workspace_any(B, d) + perm_x_bytes(B, in);
 }
 
 q4_status q4_gemm_perm(const void* x, int64_t B, const void* packed, const void* scales, const int32_t* perm,

@@ -1316,7 +1316,7 @@ hipError_t launch_gemv_stream_t(const GemmArgs& a, hipStream_t stream) {
   const int CH = S / kUnitBlocks;
   // the burst form where its conditions hold (same grid, units and result bits)
   constexpr bool kBurstKind = R == 2 && GSUB == 1 && !ASYM;
-  const bool burst = kBurstKind && J == 1 && nRB <= device_cu_count_cached();  // <= 1 workgroup per CU
+  const bool burst = kBurstKind && gemv_stream_burst_ok(a.Np, a.group, a.asym, a.q8, device_cu_count_cached());
   const void* fn = burst ? reinterpret_cast<const void*>(&gemv_stream_burst_kernel<BMAX>)
                          : reinterpret_cast<const void*>(&gemv_stream_kernel<R, GSUB, ASYM, P, BMAX>);
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
@@ -1373,7 +1373,9 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
       default: return launch_gemv_x<4, 1, false, true>(a, stream);
     }
   }
-  if (gemv_streams_x(a.B, a.Kp, a.rows_per_wave, a.k_splits)) return launch_gemv_stream_a<2>(a, stream);
+  if (gemv_streams_x(a.B, a.Kp, a.rows_per_wave, a.k_splits,
+                     gemv_stream_burst_ok(a.Np, a.group, a.asym, a.q8, device_cu_count_cached())))
+    return launch_gemv_stream_a<2>(a, stream);
   switch (a.rows_per_wave) {
     case 1: return launch_gemv_a<1>(a, stream);
     case 2: return launch_gemv_a<2>(a, stream);

@@ -113,11 +113,21 @@ constexpr size_t mfma_lds_bytes(int col_tiles) {
   return (size_t)2 * col_tiles * 16 * (mfma_chunk_blocks(col_tiles) * 128 + kGemmRowPad) * 2;
 }
 
-// Whether the GEMV for this shape streams x per unit (B <= 3, one split, two row
-// tiles per wavefront, a multiple of 1024 channels) instead of staging the whole slice.
-inline bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits) {
+// Whether the streaming GEMV runs in its burst form (gemv_stream_burst_kernel): symmetric
+// INT4 codes, groups of 128, and at most one workgroup per CU (row blocks of two tiles
+// <= CUs), the grid its register budget allows.
+inline bool gemv_stream_burst_ok(int Np, int group, bool asym, bool q8, int cus) {
+  return !asym && !q8 && group == 128 && (Np / 16 + 1) / 2 <= cus;
+}
+
+// Whether the GEMV for this shape streams x per unit (one split, two row tiles per
+// wavefront, a multiple of 1024 channels; B <= 3, or B = 4 in the burst form: there the
+// per-unit activation loads measured 0.3-0.7 us faster than the staged launch on o,
+// down and 8192x14336) instead of staging the whole slice.
+inline bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits, bool burst_form) {
   const int S = Kp / 128;
-  return B >= 1 && B <= 3 && k_splits == 1 && rows_per_wave == 2 && S % kStreamUnitBlocks == 0;
+  return B >= 1 && (B <= 3 || (B == 4 && burst_form)) && k_splits == 1 && rows_per_wave == 2 &&
+         S % kStreamUnitBlocks == 0;
 }
 // Facts of the current device, each looked up once per device and kept in one
 // lock-guarded cache (q4_api.cpp): its compute units, the workgroups of `block`
