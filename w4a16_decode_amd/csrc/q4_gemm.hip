@@ -1257,6 +1257,18 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   CH = std::min(CH, 64);
   CH = (int)std::min<int64_t>(CH, std::max<int64_t>(1, (int64_t)((lim - std::min(lim, base)) / (unit_bytes * n_rb))));
   CH = std::max(CH, 1);
+  if (burst && min_nsb % 4 == 0 && min_nsb % (4 * CH) != 0) {
+    // the burst kernel needs units of whole 4-block bursts: the next larger CH that
+    // divides the split's bursts (shorter units) where its partials fit the LDS
+    const int bursts = min_nsb / 4;
+    const int64_t ch_max = std::min<int64_t>(
+        64, std::max<int64_t>(1, (int64_t)((lim - std::min(lim, base)) / (unit_bytes * n_rb))));
+    for (int d = CH + 1; d <= bursts && d <= ch_max; ++d)
+      if (bursts % d == 0) {
+        CH = d;
+        break;
+      }
+  }
   const size_t lds = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, n_rb * CH).total;
   const int grid = (int)(per_split * KS);
   if constexpr (kBurstKind) {
