@@ -413,20 +413,23 @@ def test_full_heavy_tailed_gemv(q4, g, asym):
     _full_size_check(q4, 14336, 4096, g, (1,), asym=asym, seed=5, heavy=True)
 
 
-# Staged one-row-tile GEMVs (gemv_burst_kernel): units of one 4-block burst (4096x4096
-# and 6144x4096 at B <= 2, 8 chunks of 32 blocks) and of several (14336x4096 at B = 4).
-# Each wavefront's first units are fixed and the LDS unit counter is read only after
-# the barrier that follows its initialisation; a product that took a unit from an
+# Burst GEMVs. Staged, one row tile per wavefront (gemv_burst_kernel): units of one
+# 4-block burst (4096x4096 and 6144x4096 at B <= 2, 8 chunks of 32 blocks) and of
+# several (14336x4096 at B = 4). Streamed, two row tiles per wavefront
+# (gemv_stream_burst_kernel: 8192x8192 at B = 1 and 4, one workgroup per CU). Each
+# wavefront's first units are fixed and the LDS unit counter is read only after the
+# barrier that follows its initialisation; a product that took a unit from an
 # uninitialised counter would skip or repeat units. The products run repeatedly with
 # a skinny GEMM between them (other data left in LDS) and must all give the bits of
 # the first, which must match the oracle.
-@pytest.mark.parametrize("N,K,B", [(4096, 4096, 1), (4096, 4096, 2), (6144, 4096, 1), (14336, 4096, 4)])
-def test_burst_gemv_units_repeatable(q4, N, K, B):
+@pytest.mark.parametrize("N,K,B,R", [(4096, 4096, 1, 1), (4096, 4096, 2, 1), (6144, 4096, 1, 1), (14336, 4096, 4, 1),
+                                     (8192, 8192, 1, 2), (8192, 8192, 4, 2)])
+def test_burst_gemv_units_repeatable(q4, N, K, B, R):
     import torch
 
     say(f"burst GEMV N={N} K={K} B={B}")
-    R, W, KS, CT = q4.gemm_shape(B, N, K, 128)
-    assert (R, KS, CT) == (1, 1, 1), (R, W, KS, CT)  # the staged one-row-tile launch
+    got = q4.gemm_shape(B, N, K, 128)
+    assert (got[0], got[2], got[3]) == (R, 1, 1), got  # one split: the staged (R = 1) or streamed (R = 2) launch
     W_ = synth.weight(N, K, seed=31)
     x = synth.activation(B, K, seed=31)
     qw = q4.quantize_pack(to_gpu(W_), 128)
