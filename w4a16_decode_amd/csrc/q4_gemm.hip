@@ -451,23 +451,25 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
 // ---------------------------------------------------------------------------------
 // GEMV for the common case of the staged kernel: symmetric INT4 codes with one scale
 // per 1 KiB block (groups of 128 channels), one row tile per wavefront, and chunks of
-// a whole number of 4-block bursts (the host checks S % KS == 0 and
-// (S / KS) % (4 CH) == 0). It runs gemv_kernel<1, 1, false, 8, XCH>'s grid, units,
-// x staging, burst ring (two halves of 4 blocks), arithmetic and final reduction, so
-// the two give identical bits; what differs is the instruction stream around the
-// loads. gemv_kernel re-derives every block's code and scale addresses from a block
+// a whole number of NB-block bursts (the host checks S % KS == 0 and
+// (S / KS) % (NB CH) == 0). It runs gemv_kernel<1, 1, false, 8, XCH>'s grid, units,
+// x staging, arithmetic and final reduction (its burst ring has two halves of NB
+// blocks: 4 as gemv_kernel's, or 2, which the host takes for rows of >= 8192
+// channels), so for the same CH the two give identical bits whatever NB (the blocks of
+// a unit are summed in the same order); what differs is the instruction stream
+// around the loads. gemv_kernel re-derives every block's code and scale addresses from a block
 // index, with clamps, a group division and a unit test per block (~40 scalar
 // instructions and several branches per 1 KiB block). Here a unit's code and scale
-// bases are formed once when the unit is taken, a burst is 4 loads from one scalar
+// bases are formed once when the unit is taken, a burst is NB loads from one scalar
 // base plus per-lane offsets held in registers (block q of a burst sits q * CH KiB
 // further), and the unit counter is read once per unit.
-template <int XCH>
+template <int XCH, int NB>  // NB: blocks per burst (2 or 4)
 __global__ __launch_bounds__(16 * 64)
 void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
                        const uint16_t* __restrict__ scales, int N, int K, int S, int Gp, int KS, int nRB, int CH,
                        uint16_t* __restrict__ y, float* __restrict__ ws) {
+  static_assert(NB == 2 || NB == 4, "bursts of 2 or 4 blocks");
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NB = 4;  // blocks per burst
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1231,8 +1233,13 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   // the burst kernel where its conditions hold (same grid, units and result bits)
   constexpr bool kBurstKind = R == 1 && GSUB == 1 && !ASYM && !Q8;
   const bool burst = kBurstKind && J == 1 && S % KS == 0;  // CH is checked below
-  const void* fn = burst ? reinterpret_cast<const void*>(&gemv_burst_kernel<XCH>)
-                         : reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>);
+  // bursts of 2 blocks on rows of >= 8192 channels (ABBA against 4 on the 70B shapes at
+  // B = 1-16: q/k/v -0.7 to -0.9 us, gate/up and 28672x8192 -0.2 to -0.7 us), of 4 on
+  // shorter ones (4096x4096 and 28672x4096 at B = 1: 0.2-0.3 us faster with 4)
+  const int NBB = S >= 64 ? 2 : 4;
+  const void* fn = !burst ? reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>)
+                   : NBB == 2 ? reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 2>)
+                              : reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 4>);
   const size_t lim = a.lds_limit;
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, 0).total;
@@ -1257,10 +1264,10 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   CH = std::min(CH, 64);
   CH = (int)std::min<int64_t>(CH, std::max<int64_t>(1, (int64_t)((lim - std::min(lim, base)) / (unit_bytes * n_rb))));
   CH = std::max(CH, 1);
-  if (burst && min_nsb % 4 == 0 && min_nsb % (4 * CH) != 0) {
-    // the burst kernel needs units of whole 4-block bursts: the next larger CH that
-    // divides the split's bursts (shorter units) where its partials fit the LDS
-    const int bursts = min_nsb / 4;
+  if (burst && min_nsb % NBB == 0 && min_nsb % (NBB * CH) != 0) {
+    // the burst kernel needs units of whole bursts: the next larger CH that divides
+    // the split's bursts (shorter units) where its partials fit the LDS
+    const int bursts = min_nsb / NBB;
     const int64_t ch_max = std::min<int64_t>(
         64, std::max<int64_t>(1, (int64_t)((lim - std::min(lim, base)) / (unit_bytes * n_rb))));
     for (int d = CH + 1; d <= bursts && d <= ch_max; ++d)
@@ -1272,11 +1279,17 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   const size_t lds = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, n_rb * CH).total;
   const int grid = (int)(per_split * KS);
   if constexpr (kBurstKind) {
-    if (burst && (S / KS) % (4 * CH) == 0) {
-      hipLaunchKernelGGL((gemv_burst_kernel<XCH>), dim3(grid), dim3(W * kWave), lds, stream,
-                         static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
-                         static_cast<const uint16_t*>(a.scales), a.N, a.K, S, a.Gp, KS, nRB, CH,
-                         static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
+    if (burst && (S / KS) % (NBB * CH) == 0) {
+      if (NBB == 2)
+        hipLaunchKernelGGL((gemv_burst_kernel<XCH, 2>), dim3(grid), dim3(W * kWave), lds, stream,
+                           static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
+                           static_cast<const uint16_t*>(a.scales), a.N, a.K, S, a.Gp, KS, nRB, CH,
+                           static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
+      else
+        hipLaunchKernelGGL((gemv_burst_kernel<XCH, 4>), dim3(grid), dim3(W * kWave), lds, stream,
+                           static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
+                           static_cast<const uint16_t*>(a.scales), a.N, a.K, S, a.Gp, KS, nRB, CH,
+                           static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
       if (KS > 1)
         launch_reduce_splits(static_cast<const float*>(a.workspace), KS, (int64_t)a.B * a.N,
                              static_cast<uint16_t*>(a.y), stream);
