@@ -212,9 +212,9 @@ void pick_shape(int B, const Dims& d, q4::GemmArgs* a) {
     int KS = 1;
     // two row tiles per wavefront at B <= 3 stream x per unit (no activation slice
     // to fit in LDS, so no channel split); otherwise the fewest splits whose slice fits
-    const bool streamed =
-        !a->q8 && q4::gemv_streams_x(B, d.Kp, R, 1,
-                                     q4::gemv_stream_burst_ok(d.Np, d.group, a->asym, a->q8, q4::device_cu_count_cached()));
+    // (B = 4 takes the model's pick below; the launch streams x where that pick is two
+    // row tiles without a split and the burst form runs)
+    const bool streamed = !a->q8 && B <= 3 && q4::gemv_streams_x(B, d.Kp, R, 1, false);
     while (!streamed && KS < S && !gemv_shape_ok(B, S, KS, W, R, d.group, a->asym, lim, a->q8)) ++KS;
     a->rows_per_wave = R;
     a->waves_per_group = W;

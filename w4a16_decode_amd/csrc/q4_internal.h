@@ -120,10 +120,11 @@ inline bool gemv_stream_burst_ok(int Np, int group, bool asym, bool q8, int cus)
   return !asym && !q8 && group == 128 && (Np / 16 + 1) / 2 <= cus;
 }
 
-// Whether the GEMV for this shape streams x per unit (one split, two row tiles per
-// wavefront, a multiple of 1024 channels; B <= 3, or B = 4 in the burst form: there the
-// per-unit activation loads measured 0.3-0.7 us faster than the staged launch on o,
-// down and 8192x14336) instead of staging the whole slice.
+// Whether the GEMV for this launch shape streams x per unit (one split, two row tiles
+// per wavefront, a multiple of 1024 channels; B <= 3, or B = 4 in the burst form, where
+// streaming measured faster than the staged kernel with two row tiles) instead of
+// staging the whole slice. The host's own pick streams at B <= 3 only; at B = 4 its
+// launch model decides the shape (streamed where that is two row tiles, no split).
 inline bool gemv_streams_x(int B, int Kp, int rows_per_wave, int k_splits, bool burst_form) {
   const int S = Kp / 128;
   return B >= 1 && (B <= 3 || (B == 4 && burst_form)) && k_splits == 1 && rows_per_wave == 2 &&

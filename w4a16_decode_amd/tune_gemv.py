@@ -83,23 +83,6 @@ def pick(N: int, K: int, B: int, coef, lds_limit: int = LDS_LIMIT, cus: int = CU
     return out
 
 
-def streams_x(N: int, K: int, B: int, cus: int = CUS) -> bool:
-    """Whether the library streams x per unit at this B >= 4 instead of taking the
-    model's pick (gemv_streams_x with gemv_stream_burst_ok in csrc/q4_internal.h, for
-    symmetric codes with g = 128): at B = 4, where the host's rule gives two row tiles
-    per wavefront, the rows are a multiple of 1024 channels and the row blocks fit one
-    workgroup per CU."""
-    T, S = -(-N // 16), -(-K // 128)
-    R = 1 if (T >= 2048 or T > S * 8 or T < 512) else 2
-    return B == 4 and R == 2 and S % 8 == 0 and (T + 1) // 2 <= cus
-
-
-def library_pick(N: int, K: int, B: int, coef, lds_limit: int = LDS_LIMIT, cus: int = CUS):
-    """The launch shape (R, W, KS) the library takes at 4 <= B <= 16: the streamed one
-    (2, 8, 1) where streams_x holds, else the model's pick."""
-    return (2, 8, 1) if streams_x(N, K, B, cus) else pick(N, K, B, coef, lds_limit, cus)
-
-
 def load(paths):
     rows = []
     for p in paths:
