@@ -1,7 +1,7 @@
 """Time two builds of libq4.so against each other, interleaved (GPU).
 
     python -m w4a16_decode_amd.compare_builds LIB_A LIB_B --batches 1,4,8 \
-        --shapes 57344x8192,8192x28672 [--rounds 8] [--group 128]
+        --shapes 57344x8192,8192x28672 [--rounds 8] [--group 128] [--q8]
 
 Both libraries are opened in one process (each through its own handle; the product
 calls of this package are pointed at one or the other in turn). For every matrix
@@ -48,6 +48,7 @@ def main(argv=None) -> int:
     ap.add_argument("--shapes", default="57344x8192")
     ap.add_argument("--rounds", type=int, default=8)
     ap.add_argument("--group", type=int, default=128)
+    ap.add_argument("--q8", action="store_true", help="per-row INT8 codes (q8_quantize_pack / q8_gemm)")
     args = ap.parse_args(argv)
 
     import torch
@@ -87,8 +88,10 @@ def main(argv=None) -> int:
         N, K = map(int, shape.split("x"))
         copies = max(2, min(16, int(1.0e9 // (N * K * 0.52))))
         use("A")
-        qws = [ops.quantize_pack(synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev), args.group)
-               for c in range(copies)]
+        copies = max(2, copies // 2) if args.q8 else copies  # INT8 codes are twice the bytes
+        quant = ops.q8_quantize_pack if args.q8 else (lambda W: ops.quantize_pack(W, args.group))
+        product = ops.q8_gemm if args.q8 else ops.gemm
+        qws = [quant(synth.device_weight(N, K, seed=4, layer=c, matrix=0, device=dev)) for c in range(copies)]
         for B in (int(b) for b in args.batches.split(",")):
             x = synth.device_activation(B, K, seed=4, layer=0, matrix=0, device=dev)
             ys = {n: torch.empty((B, N), dtype=torch.float16, device=dev) for n in libs}
@@ -96,7 +99,7 @@ def main(argv=None) -> int:
             graphs = {}
             for n in libs:
                 use(n)
-                graphs[n] = graph_of(lambda: [ops.gemm(x, qw, out=ys[n], workspace=wss[n]) for qw in qws])
+                graphs[n] = graph_of(lambda: [product(x, qw, out=ys[n], workspace=wss[n]) for qw in qws])
             if not warmed:
                 for _ in range(60):
                     for n in libs:

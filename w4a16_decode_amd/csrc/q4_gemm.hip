@@ -463,13 +463,16 @@ void gemv_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict_
 // bases are formed once when the unit is taken, a burst is NB loads from one scalar
 // base plus per-lane offsets held in registers (block q of a burst sits q * CH KiB
 // further), and the unit counter is read once per unit.
-template <int XCH, int NB>  // NB: blocks per burst (2 or 4)
+template <int XCH, int NB, bool Q8 = false>  // NB: blocks per burst (2 or 4); Q8: INT8 codes
 __global__ __launch_bounds__(16 * 64)
 void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __restrict__ packed,
                        const uint16_t* __restrict__ scales, int N, int K, int S, int Gp, int KS, int nRB, int CH,
                        uint16_t* __restrict__ y, float* __restrict__ ws) {
   static_assert(NB == 2 || NB == 4, "bursts of 2 or 4 blocks");
   extern __shared__ __align__(16) unsigned char smem[];
+  // INT8 codes (W8A16): 2 KiB blocks of two 16-byte pieces per lane, one scale per row
+  constexpr int NW = Q8 ? 2 : 1;
+  constexpr uint32_t BLKB = 1024u * NW;
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -504,8 +507,8 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
   // of a burst are fixed registers, the burst's scalar base moves by NB * CH blocks.
   const unsigned char* pk = reinterpret_cast<const unsigned char*>(packed);
   const unsigned char* sk = reinterpret_cast<const unsigned char*>(scales);
-  const uint32_t cstride = (uint32_t)CH * 1024u;  // bytes between a unit's blocks (codes)
-  const uint32_t sstride = (uint32_t)CH * 32u;    // ... (scales: 16 float16 per block)
+  const uint32_t cstride = (uint32_t)CH * BLKB;        // bytes between a unit's blocks (codes)
+  const uint32_t sstride = Q8 ? 0u : (uint32_t)CH * 32u;  // ... (scales: 16 float16 per block; per row for INT8)
   uint32_t woff[NB], soff[NB], lw[NB], ls[NB];  // lw, ls: the offsets loads use now
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
@@ -548,8 +551,8 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
     const int i = u / CH;
     c_chunk = u - i * CH;
     const size_t tile = (size_t)(rb_first + i * rb_stride);
-    c_w = pk + (tile * S + wsb0 + c_chunk) * 1024;
-    c_s = sk + (tile * Gp + wsb0 + c_chunk) * 32;
+    c_w = pk + (tile * S + wsb0 + c_chunk) * BLKB;
+    c_s = sk + (tile * Gp + (Q8 ? 0 : wsb0 + c_chunk)) * 32;
   };
   if (threadIdx.x == 0) *counter = KST * W * 64;
   take();
@@ -557,20 +560,23 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
   // one burst in flight: codes and scales of NB blocks, the unit and chunk they
   // belong to, the index of the burst's first block in the unit and whether it ends it
   struct Burst {
-    uint4 w[NB];
+    uint4 w[NB][NW];
     uint2 sc[NB];
     int unit, chunk, j0;
     bool last;
   };
   auto issue = [&](Burst& b) __attribute__((always_inline)) {
     const size_t boff = (size_t)c_burst * NB * CH;
-    const unsigned char* wb = c_w + boff * 1024;
-    const unsigned char* sb = c_s + boff * 32;
+    const unsigned char* wb = c_w + boff * BLKB;
+    const unsigned char* sb = c_s + (Q8 ? 0 : boff * 32);
     // codes and scale of one block after the other: loads complete in order, so
     // block q waits for the first 2 (q + 1) loads of the burst only
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      b.w[q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb + lw[q])));
+#pragma unroll
+      for (int h = 0; h < NW; ++h)
+        b.w[q][h] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb + lw[q] + 1024u * h)));
       b.sc[q] = *reinterpret_cast<const uint2*>(sb + ls[q]);
     }
     b.unit = c_unit;
@@ -585,7 +591,7 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
 
   // 3. x slice -> LDS, plus the zero row and the per-unit biases
   const int nunits = nsb;
-  gemv_store_x<XCH, true, false, kSuperK>(xr, xl, xzero, beta, B, K, wsb0, row_chunks, nunits);
+  gemv_store_x<XCH, true, Q8, kSuperK>(xr, xl, xzero, beta, B, K, wsb0, row_chunks, nunits);
   lds_barrier();
 
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -624,8 +630,16 @@ void gemv_burst_kernel(const uint16_t* __restrict__ x, int B, const uint4* __res
       read_x(q + 1 < NB ? block_of(b, q + 1) : block_of(nx, 0));
       const half4_t sh = __builtin_bit_cast(half4_t, b.sc[q]);
       float4_t part = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (Q8) {
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) part = mfma16x16x32(magic8r(lane_dword(b.w[q], mm), dq), xc[mm], part);
+        for (int mm = 0; mm < 4; ++mm) {
+          const uint4& v = b.w[q][mm >> 1];
+          part = mfma16x16x32(magic8_i8(lane_dword(v, 2 * (mm & 1)), lane_dword(v, 2 * (mm & 1) + 1)), xc[mm], part);
+        }
+      } else {
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) part = mfma16x16x32(magic8r(lane_dword(b.w[q][0], mm), dq), xc[mm], part);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf((float)sh[i], part[i] - bc, acc[i]);
     }
@@ -1231,15 +1245,16 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   const int max_nsb = (S + KS - 1) / KS;
   const int min_nsb = S / KS;  // >= 1: the host keeps KS <= S
   // the burst kernel where its conditions hold (same grid, units and result bits)
-  constexpr bool kBurstKind = R == 1 && GSUB == 1 && !ASYM && !Q8;
-  const bool burst = kBurstKind && J == 1 && S % KS == 0;  // CH is checked below
+  constexpr bool kBurstKind = R == 1 && GSUB == 1 && !ASYM;
+  const bool burst = kBurstKind && (Q8 || J == 1) && S % KS == 0;  // CH is checked below (INT8: one group per row)
   // bursts of 2 blocks on rows of >= 8192 channels (ABBA against 4 on the 70B shapes at
   // B = 1-16: q/k/v -0.7 to -0.9 us, gate/up and 28672x8192 -0.2 to -0.7 us), of 4 on
   // shorter ones (4096x4096 and 28672x4096 at B = 1: 0.2-0.3 us faster with 4)
-  const int NBB = S >= 64 ? 2 : 4;
+  // (INT8 blocks are 2 KiB: bursts of 2 blocks always)
+  const int NBB = (Q8 || S >= 64) ? 2 : 4;
   const void* fn = !burst ? reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>)
-                   : NBB == 2 ? reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 2>)
-                              : reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 4>);
+                   : NBB == 2 ? reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 2, Q8>)
+                              : reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 4, Q8>);
   const size_t lim = a.lds_limit;
   const size_t unit_bytes = (size_t)R * 16 * a.B * 4;
   const size_t base = GemvLds(a.B, max_nsb, GSUB, !ASYM, R, 0).total;
@@ -1281,12 +1296,12 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   if constexpr (kBurstKind) {
     if (burst && (S / KS) % (NBB * CH) == 0) {
       if (NBB == 2)
-        hipLaunchKernelGGL((gemv_burst_kernel<XCH, 2>), dim3(grid), dim3(W * kWave), lds, stream,
+        hipLaunchKernelGGL((gemv_burst_kernel<XCH, 2, Q8>), dim3(grid), dim3(W * kWave), lds, stream,
                            static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                            static_cast<const uint16_t*>(a.scales), a.N, a.K, S, a.Gp, KS, nRB, CH,
                            static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
       else
-        hipLaunchKernelGGL((gemv_burst_kernel<XCH, 4>), dim3(grid), dim3(W * kWave), lds, stream,
+        hipLaunchKernelGGL((gemv_burst_kernel<XCH, 4, Q8>), dim3(grid), dim3(W * kWave), lds, stream,
                            static_cast<const uint16_t*>(a.x), a.B, static_cast<const uint4*>(a.packed),
                            static_cast<const uint16_t*>(a.scales), a.N, a.K, S, a.Gp, KS, nRB, CH,
                            static_cast<uint16_t*>(a.y), static_cast<float*>(a.workspace));
