@@ -1247,11 +1247,12 @@ hipError_t launch_gemv_t(const GemmArgs& a, hipStream_t stream) {
   // the burst kernel where its conditions hold (same grid, units and result bits)
   constexpr bool kBurstKind = R == 1 && GSUB == 1 && !ASYM;
   const bool burst = kBurstKind && (Q8 || J == 1) && S % KS == 0;  // CH is checked below (INT8: one group per row)
-  // bursts of 2 blocks on rows of >= 8192 channels (ABBA against 4 on the 70B shapes at
-  // B = 1-16: q/k/v -0.7 to -0.9 us, gate/up and 28672x8192 -0.2 to -0.7 us), of 4 on
-  // shorter ones (4096x4096 and 28672x4096 at B = 1: 0.2-0.3 us faster with 4)
+  // bursts of 2 blocks on rows of >= 8192 channels and from B = 4 up (ABBA against 4: q/k/v
+  // of the 70B layer -0.7 to -0.9 us at B = 1-16, gate/up and 28672x8192 -0.2 to -0.7 us;
+  // 4096-channel rows of the 8B layer -0.3 to -1.0 us at B = 4-8), of 4 on shorter rows at
+  // B <= 3 (4096x4096, 6144x4096 and 28672x4096 at B = 1: 0.2-0.4 us faster with 4)
   // (INT8 blocks are 2 KiB: bursts of 2 blocks always)
-  const int NBB = (Q8 || S >= 64) ? 2 : 4;
+  const int NBB = (Q8 || S >= 64 || a.B >= 4) ? 2 : 4;
   const void* fn = !burst ? reinterpret_cast<const void*>(&gemv_kernel<R, GSUB, ASYM, P, XCH, Q8>)
                    : NBB == 2 ? reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 2, Q8>)
                               : reinterpret_cast<const void*>(&gemv_burst_kernel<XCH, 4, Q8>);
